@@ -1,0 +1,234 @@
+"""Throughput of the FP8 W8A8 linear on one MI355X.
+
+One step = the whole per-call hot path on one batch: dynamic per-token e4m3fn
+quantisation of the bf16 activation, then the FP8 GEMM with the fused
+activation-scale x weight-scale, bias and bf16 epilogue (two launches on one
+stream). The workload is the FFN-up linear of the HunyuanVideo1.5 DiT
+(M=4096 tokens, N=8192, K=2048). The weight is quantised per output channel and
+the plan built before timing (construction-time work, as the method prescribes).
+
+Inputs, weights and outputs rotate over enough independent sets (> 1 GiB in
+total) that no step finds its operands in the 256 MB last-level cache; every
+operand is resident in HBM when the timed region starts.
+
+Prints one JSON line. `value` = 2 M N K / step time (TFLOP/s). `roofline` is the
+GEMM kernel (the dominant launch), timed with HIP events recorded on the launch
+stream around every launch inside the timed region. `cpu_baseline` times the CPU
+oracle (numpy, float64) on the same workload.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 W8A8 linear TFLOP/s (quant+GEMM+epilogue), M4096 N8192 K2048; quant GB/s"
+M, N, K = 4096, 8192, 2048
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_ffn_up_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", "gemm_fp8.hip")
+
+
+def gemm_bytes(m, n, k):
+    # q8 A, q8 W, bf16 out, fp32 a-scale, fp32 w-scale, bf16 bias
+    return m * k + n * k + 2 * m * n + 4 * m + 4 * n + 2 * n
+
+
+def quant_bytes(m, k):
+    return 3 * m * k + 4 * m  # read bf16, write codes and fp32 scales
+
+
+def traffic_from_profile():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if t.get("gemm_source_sha256") != src:
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(budget_s=20.0):
+    """The CPU oracle (as it stands) on the FFN-up workload: quant + exact float64 linear."""
+    import numpy as np
+    from oracle import linear as ol, quant as oq
+    from workloads import bf16_bits, make_config
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    cfg = make_config("ffn_up")
+    a = bf16_bits(cfg["activations"]["a"])
+    w = bf16_bits(cfg["weights"]["ffn_up"])
+    b = bf16_bits(cfg["biases"]["ffn_up"])
+    qw, sw = oq.quant_weights_per_channel(w)  # construction-time, not timed
+    # bounded sample: the first R rows of the activation, R chosen from a trial run
+    rows = 256
+    t0 = time.perf_counter()
+    ol.linear_ref(a[:rows], qw, sw, b)
+    t_trial = time.perf_counter() - t0
+    rows = int(min(M, max(256, rows * budget_s / 3 / max(t_trial, 1e-3))))
+    best = None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ol.linear_ref(a[:rows], qw, sw, b)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    tflops = 2.0 * rows * N * K / best / 1e12
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": blas_threads or cores,
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} token rows of the FFN-up workload (N={N}, K={K}): numpy per-token quant "
+                  f"(1 core) + float64 exact dequantised matmul (BLAS threads={blas_threads}, affinity {cores} "
+                  f"cores) + epilogue; best of 3, {best:.2f} s each; scaled to TFLOP/s by 2*rows*N*K",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(tokens would shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_w8a8_quantized_token_amd as fp8
+    from fp8_w8a8_quantized_token_amd import _lib
+    from workloads.synth import activation, bias as gen_bias, outlier_channels, weight
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda", 0)
+    lib = _lib.lib()
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # rotating sets: activation bf16, codes + scales, weight plan, output
+    sets = []
+    ch = outlier_channels(0, 2, 0, K, None)
+    for i in range(args.sets):
+        a = activation(0, 2, 10 + i, M, K, "outlier", ch).to(dev)
+        w = weight(0, 2, 100 + i, N, K).to(dev)
+        b = gen_bias(0, 2, 200 + i, N).to(dev)
+        lin = fp8.Fp8Linear(w, b)  # per-channel weight quant + plan: construction time
+        del w
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        s = torch.empty((M,), dtype=torch.float32, device=dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sets.append((a, q, s, lin, out))
+    torch.cuda.synchronize()
+    config = sets[0][3].config(M)
+
+    def step(i, ev=None):
+        a, q, s, lin, out = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.fp8_quant_rows(ctypes.c_void_p(a.data_ptr()), M, K, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(s.data_ptr()), sptr)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
+        if ev is not None:
+            ev[1].record(stream)
+        st = lib.fp8_linear_run(lin._plan, M, ctypes.c_void_p(q.data_ptr()), _lib.A_E4M3,
+                                ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(out.data_ptr()), None, 0, sptr)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    quant_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    gemm_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    q_avg = sum(quant_ms) / len(quant_ms)
+    g_avg = sum(gemm_ms) / len(gemm_ms)
+    flop = 2.0 * M * N * K
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flop / (g_avg * 1e-3) / 1e12
+    traffic = traffic_from_profile()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {
+            "workload": "FFN-up linear M4096 N8192 K2048: bf16 activation N(0,1) with 1% channels x50 -> "
+                        "per-token e4m3fn quant -> FP8 GEMM vs per-channel e4m3fn weight N(0,1/sqrt(2048)) "
+                        "-> x a_scale x w_scale + bf16 bias -> bf16",
+            "M": M, "N": N, "K": K,
+            "rotating_sets": args.sets,
+            "gemm_config": {"id": config[0], "tile_m": config[1], "tile_n": config[2], "workgroups": config[3]},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_fp8_kernel",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(g_avg * 1e3, 3),
+            "algorithmic_flop_per_launch": flop,
+            "algorithmic_bytes_per_launch": gemm_bytes(M, N, K),
+        },
+        "quant": {
+            "kernel": "quant_rows_regs",
+            "avg_launch_us": round(q_avg * 1e3, 3),
+            "median_launch_us": round(quant_ms[len(quant_ms) // 2] * 1e3, 3),
+            "gbps": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9, 1),
+            "frac_hbm": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes_per_launch": quant_bytes(M, K),
+        },
+        "gemm_median_us": round(gemm_ms[len(gemm_ms) // 2] * 1e3, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

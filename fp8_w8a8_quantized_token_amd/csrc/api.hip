@@ -1,0 +1,288 @@
+// C ABI of libfp8w8a8: argument checks, the construction-time plan and its
+// shape-keyed kernel selector, and the launch sequence of a forward.
+//
+// The HunyuanVideo1.5 BF16->FP8 retrospective (aigcage.com, section 3.3) moves
+// every generic decision (input kind checks, "is the native op loaded", "which
+// backend suits this shape", "fall back to torch?") out of the per-layer forward
+// and into construction. Here: fp8_linear_create validates the weight, checks
+// the device once and picks a GEMM configuration per activation-row bucket from
+// (n, k, compute units); fp8_linear_run does O(1) argument checks, one bucket
+// lookup and two launches. There is no fallback path of any kind.
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "internal.h"
+
+using namespace fp8w8a8;
+
+struct fp8_linear_plan {
+  int device;
+  int64_t n, k;
+  const uint8_t* w;
+  const float* w_scale;
+  const uint16_t* bias;
+  int cu_count;
+  // m buckets: rows <= max_m[b] use config[b]; the last bucket is unbounded
+  static constexpr int kBuckets = 6;
+  int64_t max_m[kBuckets];
+  int config[kBuckets];
+};
+
+namespace {
+
+constexpr int64_t kMaxWorkgroupThreads = 256;
+constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device "is gfx950" and compute-unit count, filled once per device ordinal.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+int query_device(int device, int* cus) {
+  if (device < 0 || device >= kMaxDevices) return FP8W8A8_ERR_BAD_DEVICE;
+  int st = g_dev_state[device].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FP8W8A8_ERR_HIP;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[device].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[device].store(st, std::memory_order_release);
+  }
+  if (cus) *cus = g_dev_cus[device].load(std::memory_order_relaxed);
+  return st == 1 ? FP8W8A8_OK : FP8W8A8_ERR_BAD_DEVICE;
+}
+
+int current_device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8W8A8_ERR_HIP;
+  return query_device(dev, nullptr);
+}
+
+int check_quant_args(const void* x, int64_t rows, int64_t cols, const void* q, const float* scale) {
+  if (!x || !q || !scale) return FP8W8A8_ERR_INVALID_ARG;
+  if (rows < 0 || rows >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (cols < 16 || cols > FP8W8A8_MAX_DIM || cols % 16 != 0) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8W8A8_ERR_MISALIGNED;
+  return FP8W8A8_OK;
+}
+
+int check_weight_args(int64_t n, int64_t k, const void* w, const float* w_scale, const void* bias) {
+  if (!w || !w_scale) return FP8W8A8_ERR_INVALID_ARG;
+  if (n < 16 || k < 16 || n > FP8W8A8_MAX_DIM || k > FP8W8A8_MAX_DIM) return FP8W8A8_ERR_BAD_SHAPE;
+  if (n % 16 != 0 || k % 16 != 0) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(w, 16) || !aligned(w_scale, 16) || (bias && !aligned(bias, 16))) return FP8W8A8_ERR_MISALIGNED;
+  return FP8W8A8_OK;
+}
+
+bool grid_fits(int config, int64_t m, int64_t n) {
+  return gemm_workgroups(config, m, n) * kMaxWorkgroupThreads < kMaxGridThreads;
+}
+
+// Relative throughput of one workgroup of each configuration when it has a CU to
+// itself, and how many of its workgroups share a CU (LDS / register bound).
+struct TileModel {
+  double eff;
+  int per_cu;
+};
+TileModel tile_model(int config) {
+  switch (config) {
+    case 0: return {1.00, 1};
+    case 1: return {0.92, 1};
+    case 2: return {0.92, 1};
+    case 3: return {0.80, 2};
+    default: return {0.45, 4};
+  }
+}
+
+// Estimated time (arbitrary units) of configuration c on an m x n output.
+double model_time(int c, int64_t m, int64_t n, int cus) {
+  const GemmConfig* g = gemm_config(c);
+  const TileModel t = tile_model(c);
+  const int64_t tiles = gemm_workgroups(c, m, n);
+  const int64_t slots = (int64_t)cus * t.per_cu;
+  const int64_t waves = (tiles + slots - 1) / slots;
+  // a wave of `per_cu` co-resident tiles costs per_cu tiles' work at the tile's efficiency
+  return (double)waves * t.per_cu * (double)g->tile_m * (double)g->tile_n / t.eff;
+}
+
+int choose_config(int64_t m, int64_t n, int cus) {
+  int best = -1;
+  double best_t = 0;
+  for (int c = 0; c < gemm_config_count(); ++c) {
+    if (!grid_fits(c, m, n)) continue;
+    const double t = model_time(c, m, n, cus);
+    if (best < 0 || t < best_t) {
+      best = c;
+      best_t = t;
+    }
+  }
+  return best < 0 ? 0 : best;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8w8a8_status_string(int status) {
+  switch (status) {
+    case FP8W8A8_OK: return "ok";
+    case FP8W8A8_ERR_INVALID_ARG: return "invalid argument: a required pointer is NULL or an enum value is unknown";
+    case FP8W8A8_ERR_BAD_SHAPE: return "bad shape: a size is out of range, empty, or not a multiple of 16";
+    case FP8W8A8_ERR_MISALIGNED: return "misaligned pointer: see the alignment rules in fp8w8a8.h";
+    case FP8W8A8_ERR_BAD_DEVICE: return "bad device: not a gfx950 (MI355X-class) GPU";
+    case FP8W8A8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small: see fp8_linear_workspace_bytes";
+    case FP8W8A8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int fp8_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, void* q_out, float* scale_out,
+                   void* stream) {
+  int st = check_quant_args(x_bf16, rows, cols, q_out, scale_out);
+  if (st != FP8W8A8_OK) return st;
+  if (rows == 0) return FP8W8A8_OK;
+  st = current_device_ok();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_quant_rows(static_cast<const uint16_t*>(x_bf16), rows, cols,
+                                   static_cast<uint8_t*>(q_out), scale_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_quant_weights_per_channel(const void* w_bf16, int64_t n, int64_t k, void* w_fp8_out,
+                                  float* w_scale_out, void* stream) {
+  if (n == 0 || k == 0) return FP8W8A8_ERR_BAD_SHAPE;
+  return fp8_quant_rows(w_bf16, n, k, w_fp8_out, w_scale_out, stream);
+}
+
+int fp8_linear_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+                      const void* bias_bf16, fp8_linear_plan** out) {
+  if (!out) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  int cus = 0;
+  st = query_device(device, &cus);
+  if (st != FP8W8A8_OK) return st;
+  fp8_linear_plan* p = static_cast<fp8_linear_plan*>(calloc(1, sizeof(fp8_linear_plan)));
+  if (!p) return FP8W8A8_ERR_HIP;
+  p->device = device;
+  p->n = n;
+  p->k = k;
+  p->w = static_cast<const uint8_t*>(w_fp8);
+  p->w_scale = w_scale;
+  p->bias = static_cast<const uint16_t*>(bias_bf16);
+  p->cu_count = cus > 0 ? cus : 256;
+  // bucket upper bounds; each bucket's choice is made at its upper bound
+  static const int64_t bounds[fp8_linear_plan::kBuckets] = {64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
+  for (int b = 0; b < fp8_linear_plan::kBuckets; ++b) {
+    p->max_m[b] = bounds[b];
+    const int64_t rep = b + 1 < fp8_linear_plan::kBuckets ? bounds[b] : 32768;
+    p->config[b] = choose_config(rep, n, p->cu_count);
+  }
+  *out = p;
+  return FP8W8A8_OK;
+}
+
+static int plan_bucket_config(const fp8_linear_plan* p, int64_t m) {
+  int b = 0;
+  while (b + 1 < fp8_linear_plan::kBuckets && m > p->max_m[b]) ++b;
+  int c = p->config[b];
+  if (!grid_fits(c, m, p->n)) c = 0;  // the largest tile launches the fewest workgroups
+  return c;
+}
+
+size_t fp8_linear_workspace_bytes(const fp8_linear_plan* plan, int64_t m) {
+  if (!plan || m <= 0) return 0;
+  return align256((size_t)m * (size_t)plan->k) + align256((size_t)m * sizeof(float));
+}
+
+int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind, const float* a_scale,
+                   void* out_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !a || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  if (a_kind != FP8W8A8_A_BF16 && a_kind != FP8W8A8_A_E4M3) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(a, 16) || !aligned(out_bf16, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (a_kind == FP8W8A8_A_E4M3) {
+    if (!a_scale) return FP8W8A8_ERR_INVALID_ARG;
+    if (!aligned(a_scale, 4)) return FP8W8A8_ERR_MISALIGNED;
+  } else {
+    if (!workspace) return FP8W8A8_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return FP8W8A8_ERR_MISALIGNED;
+    if (workspace_bytes < fp8_linear_workspace_bytes(plan, m)) return FP8W8A8_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (m == 0) return FP8W8A8_OK;
+  const int config = plan_bucket_config(plan, m);
+  if (!grid_fits(config, m, plan->n)) return FP8W8A8_ERR_BAD_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* qa = static_cast<const uint8_t*>(a);
+  const float* sa = a_scale;
+  if (a_kind == FP8W8A8_A_BF16) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* ws_scale = reinterpret_cast<float*>(ws + align256((size_t)m * (size_t)plan->k));
+    hipError_t e = launch_quant_rows(static_cast<const uint16_t*>(a), m, plan->k, ws, ws_scale, s);
+    if (e != hipSuccess) return FP8W8A8_ERR_HIP;
+    qa = ws;
+    sa = ws_scale;
+  }
+  hipError_t e = launch_gemm(config, m, plan->n, plan->k, qa, sa, plan->w, plan->w_scale, plan->bias,
+                             static_cast<uint16_t*>(out_bf16), s);
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+void fp8_linear_destroy(fp8_linear_plan* plan) { free(plan); }
+
+int fp8_linear(const void* a, int a_kind, const float* a_scale, int64_t m, int64_t n, int64_t k,
+               const void* w_fp8, const float* w_scale, const void* bias_bf16, void* out_bf16,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8W8A8_ERR_HIP;
+  fp8_linear_plan* p = nullptr;
+  st = fp8_linear_create(dev, n, k, w_fp8, w_scale, bias_bf16, &p);
+  if (st != FP8W8A8_OK) return st;
+  st = fp8_linear_run(p, m, a, a_kind, a_scale, out_bf16, workspace, workspace_bytes, stream);
+  fp8_linear_destroy(p);
+  return st;
+}
+
+int fp8_linear_plan_config(const fp8_linear_plan* plan, int64_t m, int* config_id, int* tile_m, int* tile_n,
+                           int64_t* workgroups) {
+  if (!plan || !config_id || !tile_m || !tile_n || !workgroups) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  const int c = plan_bucket_config(plan, m > 0 ? m : 1);
+  const GemmConfig* g = gemm_config(c);
+  *config_id = c;
+  *tile_m = g->tile_m;
+  *tile_n = g->tile_n;
+  *workgroups = m > 0 ? gemm_workgroups(c, m, plan->n) : 0;
+  return FP8W8A8_OK;
+}
+
+int fp8_gemm_config_count(void) { return gemm_config_count(); }
+
+int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* qa, const float* a_scale,
+                        const void* w_fp8, const float* w_scale, const void* bias_bf16, void* out_bf16,
+                        void* stream) {
+  if (config_id < 0 || config_id >= gemm_config_count()) return FP8W8A8_ERR_INVALID_ARG;
+  if (!qa || !a_scale || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(qa, 16) || !aligned(out_bf16, 16) || !aligned(a_scale, 4)) return FP8W8A8_ERR_MISALIGNED;
+  if (m == 0) return FP8W8A8_OK;
+  if (!grid_fits(config_id, m, n)) return FP8W8A8_ERR_BAD_SHAPE;
+  st = current_device_ok();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_gemm(config_id, m, n, k, static_cast<const uint8_t*>(qa), a_scale,
+                             static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
+                             static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal declarations shared by the HIP translation units of libfp8w8a8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8w8a8.h"
+
+namespace fp8w8a8 {
+
+// Launch the per-row quantiser: q[r, :] = e4m3fn(x[r, :] / s[r]), s[r] = amax_r / 448.
+// Arguments are already validated (cols % 16 == 0, 16-byte aligned pointers, rows > 0).
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                             hipStream_t stream);
+
+// One compiled GEMM kernel configuration.
+struct GemmConfig {
+  int id;
+  int tile_m;   // block rows along m (activation rows)
+  int tile_n;   // block columns along n (weight rows / output channels)
+  const char* name;
+};
+
+int gemm_config_count();
+const GemmConfig* gemm_config(int id);
+
+// Workgroups a configuration launches for an m x n output.
+int64_t gemm_workgroups(int id, int64_t m, int64_t n);
+
+// Launch configuration `id` for out[m, n] = epilogue(qa[m, k] x qw[n, k]^T).
+hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* qa, const float* a_scale,
+                       const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
+                       hipStream_t stream);
+
+}  // namespace fp8w8a8

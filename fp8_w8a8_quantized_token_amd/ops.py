@@ -1,0 +1,189 @@
+"""Python binding of libfp8w8a8: torch tensors in, torch tensors out.
+
+Every function marshals arguments (device pointers, sizes, the current HIP stream)
+and calls the C ABI; all arithmetic happens in the library's HIP kernels. torch is
+used for device memory and streams only. Shapes follow include/fp8w8a8.h:
+activations [m, k] (leading dims are flattened), weights [n, k] k-contiguous
+(nn.Linear layout), outputs [m, n] bf16.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import A_BF16, A_E4M3, check, lib
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require(t, dtypes, name, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the HIP library is the only implementation)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _codes(t):
+    """View e4m3fn codes as uint8 (float8_e4m3fn tensors and uint8 tensors are accepted)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
+def quant_rows(x):
+    """Per-token quantisation of bf16 x [..., k] -> (codes uint8 [m, k], scales fp32 [m])."""
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    _require(x2, (torch.bfloat16,), "x", 2)
+    m, k = x2.shape
+    q = torch.empty((m, k), dtype=torch.uint8, device=x2.device)
+    s = torch.empty((m,), dtype=torch.float32, device=x2.device)
+    check(lib().fp8_quant_rows(_ptr(x2), m, k, _ptr(q), _ptr(s), _stream(x2)), "fp8_quant_rows")
+    return q, s
+
+
+def quant_weights_per_channel(w):
+    """Per-output-channel quantisation of an nn.Linear weight bf16 [n, k] -> (codes [n, k], scales [n])."""
+    _require(w, (torch.bfloat16,), "w", 2)
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float32, device=w.device)
+    check(lib().fp8_quant_weights_per_channel(_ptr(w), n, k, _ptr(q), _ptr(s), _stream(w)),
+          "fp8_quant_weights_per_channel")
+    return q, s
+
+
+class Fp8Linear:
+    """An FP8 W8A8 linear bound at construction (weight quantised once, GEMM config chosen once).
+
+    Construction follows the HunyuanVideo1.5 retrospective (aigcage.com, section 3.3):
+    the weight is quantised per output channel and kept in its [n, k] layout, and the
+    library picks the kernel configuration from the weight shape and the device. The
+    forward is narrow: a bf16 input is quantised per token and multiplied; an input that
+    is already e4m3fn (with its per-token scale) goes straight to the GEMM (section 3.5).
+    """
+
+    def __init__(self, weight=None, bias=None, *, w_fp8=None, w_scale=None):
+        if weight is not None:
+            if w_fp8 is not None or w_scale is not None:
+                raise ValueError("pass either a bf16 weight or (w_fp8, w_scale), not both")
+            w_fp8, w_scale = quant_weights_per_channel(weight)
+        if w_fp8 is None or w_scale is None:
+            raise ValueError("Fp8Linear needs a bf16 weight or a pre-quantised (w_fp8, w_scale)")
+        w_fp8 = _codes(w_fp8)
+        _require(w_fp8, (torch.uint8,), "w_fp8", 2)
+        _require(w_scale, (torch.float32,), "w_scale", 1)
+        n, k = w_fp8.shape
+        if w_scale.shape[0] != n:
+            raise ValueError("w_scale must have one entry per output channel")
+        if bias is not None:
+            _require(bias, (torch.bfloat16,), "bias", 1)
+            if bias.shape[0] != n:
+                raise ValueError("bias must have one entry per output channel")
+        self.w_fp8, self.w_scale, self.bias = w_fp8, w_scale, bias  # the plan borrows these
+        self.n, self.k = n, k
+        self.device = w_fp8.device
+        plan = ctypes.c_void_p()
+        check(lib().fp8_linear_create(self.device.index or 0, n, k, _ptr(w_fp8), _ptr(w_scale), _ptr(bias),
+                                      ctypes.byref(plan)), "fp8_linear_create")
+        self._plan = plan
+        self._lib = lib()
+
+    def __del__(self):
+        plan = getattr(self, "_plan", None)
+        if plan is not None and plan.value:
+            self._lib.fp8_linear_destroy(plan)
+            self._plan = None
+
+    def config(self, m):
+        """(config_id, tile_m, tile_n, workgroups) the plan launches for m activation rows."""
+        cid, tm, tn, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+        check(lib().fp8_linear_plan_config(self._plan, m, ctypes.byref(cid), ctypes.byref(tm), ctypes.byref(tn),
+                                           ctypes.byref(wg)), "fp8_linear_plan_config")
+        return cid.value, tm.value, tn.value, wg.value
+
+    def workspace_bytes(self, m):
+        return lib().fp8_linear_workspace_bytes(self._plan, m)
+
+    def forward(self, x, x_scale=None, out=None, workspace=None):
+        """out [..., n] bf16 from x [..., k] (bf16, or e4m3fn codes with x_scale [m])."""
+        lead = x.shape[:-1]
+        if x.shape[-1] != self.k:
+            raise ValueError(f"input has {x.shape[-1]} features, the weight expects {self.k}")
+        fp8_in = x.dtype in (torch.float8_e4m3fn, torch.uint8)
+        x2 = _codes(x).reshape(-1, self.k).contiguous()
+        m = x2.shape[0]
+        if fp8_in:
+            if x_scale is None:
+                raise ValueError("an e4m3fn input needs its per-token scale")
+            _require(x2, (torch.uint8,), "x", 2)
+            _require(x_scale, (torch.float32,), "x_scale", 1)
+            if x_scale.shape[0] != m:
+                raise ValueError("x_scale must have one entry per token")
+            kind, ws, ws_bytes = A_E4M3, None, 0
+        else:
+            _require(x2, (torch.bfloat16,), "x", 2)
+            kind = A_BF16
+            ws_bytes = self.workspace_bytes(m)
+            if workspace is None:
+                workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=x2.device)
+            ws = workspace
+        if out is None:
+            out = torch.empty((m, self.n), dtype=torch.bfloat16, device=x2.device)
+        else:
+            _require(out, (torch.bfloat16,), "out")
+            if out.numel() != m * self.n:
+                raise ValueError("out has the wrong size")
+        check(lib().fp8_linear_run(self._plan, m, _ptr(x2), kind, _ptr(x_scale) if fp8_in else None, _ptr(out),
+                                   _ptr(ws), ws_bytes if ws is None else ws.numel(), _stream(x2)),
+              "fp8_linear_run")
+        return out.reshape(*lead, self.n)
+
+    __call__ = forward
+
+
+def linear(a, w_fp8, w_scale, bias=None, a_scale=None):
+    """One-shot FP8 linear (creates, runs and frees a plan): out [m, n] bf16."""
+    return Fp8Linear(w_fp8=w_fp8, w_scale=w_scale, bias=bias).forward(a, a_scale)
+
+
+def gemm_config_count():
+    return lib().fp8_gemm_config_count()
+
+
+def gemm_run_config(config_id, qa, a_scale, w_fp8, w_scale, bias=None, out=None):
+    """Launch one named GEMM configuration on already-quantised operands (tests)."""
+    qa, w_fp8 = _codes(qa), _codes(w_fp8)
+    _require(qa, (torch.uint8,), "qa", 2)
+    _require(w_fp8, (torch.uint8,), "w_fp8", 2)
+    _require(a_scale, (torch.float32,), "a_scale", 1)
+    _require(w_scale, (torch.float32,), "w_scale", 1)
+    m, k = qa.shape
+    n = w_fp8.shape[0]
+    if w_fp8.shape[1] != k or a_scale.shape[0] != m or w_scale.shape[0] != n:
+        raise ValueError("operand shapes do not agree")
+    if bias is not None:
+        _require(bias, (torch.bfloat16,), "bias", 1)
+        if bias.shape[0] != n:
+            raise ValueError("bias must have n entries")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=qa.device)
+    check(lib().fp8_gemm_run_config(config_id, m, n, k, _ptr(qa), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
+                                    _ptr(bias), _ptr(out), _stream(qa)), "fp8_gemm_run_config")
+    return out
+
+
+__all__ = ["quant_rows", "quant_weights_per_channel", "Fp8Linear", "linear", "gemm_config_count",
+           "gemm_run_config", "A_BF16", "A_E4M3", "_lib"]

@@ -1,0 +1,195 @@
+/*
+ * fp8w8a8.h - C ABI of the MI355X (gfx950) FP8 W8A8 linear layer.
+ *
+ * What it computes (HunyuanVideo1.5 BF16->FP8 retrospective, aigcage.com/blog/
+ * hunyuanvideo-fp8, section 3.1): a bf16 activation is quantised per token at
+ * run time to FP8 E4M3 ("float8_e4m3fn"), multiplied on the matrix cores by a
+ * weight that was quantised per output channel ahead of time (section 2 of the
+ * same page), and the epilogue applies the activation scale, the weight scale
+ * and the bias and writes bf16.
+ *
+ *   s[m]      = fl32(max_k |A[m,k]| / 448)                   (0 for an all-zero row)
+ *   qA[m,k]   = e4m3fn_rne_sat(fl32(A[m,k] / s[m]))          (signed zero when s[m] == 0)
+ *   out[m,n]  = bf16_rne( fl32( sum_k dec(qA[m,k]) * dec(qW[n,k]) ) * s[m] * sW[n] + bias[n] )
+ *
+ * The product accumulates in fp32 on the MFMA units; the epilogue runs in fp32
+ * and rounds once to bf16 (round to nearest even). e4m3fn is the OCP 8-bit E4M3
+ * encoding: bias 7, largest finite 448, no infinity, 0x7F/0xFF NaN. Quantisation
+ * saturates at +-448 and rounds to nearest, ties to even.
+ *
+ * Layouts. Every matrix is dense, row-major, last index fastest:
+ *   A bf16 [m, k], qA u8 [m, k], W bf16 [n, k], qW u8 [n, k], out bf16 [m, n].
+ *   The weight keeps nn.Linear's [n, k] layout with k contiguous (the section's
+ *   "column-major B"); it is never transposed or copied into another layout.
+ *   Scales are fp32: s [m], sW [n]. bias is bf16 [n] or NULL.
+ *
+ * Ownership. The caller allocates and frees every device buffer. The library
+ * never allocates device memory. A plan is a small host object owned by the
+ * library (create / destroy); it borrows the weight, weight-scale and bias
+ * pointers, which must stay valid while the plan is used.
+ *
+ * Streams. Every launch is asynchronous on the caller's hipStream_t (NULL is
+ * the default stream); the library never synchronises. A plan is immutable
+ * after create, so runs on different streams may use it concurrently.
+ *
+ * Errors. Functions return FP8W8A8_OK (0) or a negative status. Arguments are
+ * checked on the host before anything is launched; nothing is printed, nothing
+ * aborts and nothing falls back to another implementation (section 3.3 of the
+ * retrospective moves such decisions out of the forward call). Device faults
+ * are asynchronous and surface at the caller's next synchronisation, as usual
+ * in HIP. Rows m == 0 are a no-op returning FP8W8A8_OK; an empty weight
+ * (n == 0 or k == 0) is FP8W8A8_ERR_BAD_SHAPE, like the "Invalid input." error
+ * that the ComfyUI FP8 quantiser page (runcomfy.com, "Quantize Model to FP8
+ * Format", common errors) gives for an empty model.
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------- */
+#define FP8W8A8_OK 0
+#define FP8W8A8_ERR_INVALID_ARG (-1)          /* a required pointer is NULL, or an unknown enum value */
+#define FP8W8A8_ERR_BAD_SHAPE (-2)            /* a size is out of range or not a multiple of 16 */
+#define FP8W8A8_ERR_MISALIGNED (-3)           /* a pointer breaks the alignment stated below */
+#define FP8W8A8_ERR_BAD_DEVICE (-4)           /* the device is not a gfx950 GPU */
+#define FP8W8A8_ERR_WORKSPACE_TOO_SMALL (-5)  /* the workspace is smaller than fp8_linear_workspace_bytes */
+#define FP8W8A8_ERR_HIP (-6)                  /* a HIP runtime call or launch failed */
+
+/* ---- activation kinds for fp8_linear_run ------------------------------------ */
+#define FP8W8A8_A_BF16 0  /* a is bf16 [m, k]; the run quantises it per token into the workspace */
+#define FP8W8A8_A_E4M3 1  /* a is already e4m3fn codes [m, k] with per-row scales a_scale [m] */
+
+/* Size limits checked by every entry point. */
+#define FP8W8A8_MAX_ROWS ((int64_t)1 << 24) /* m (or rows) must be below this */
+#define FP8W8A8_MAX_DIM ((int64_t)1 << 20)  /* n, k and cols must not exceed this */
+
+/* Human-readable text of a status code (a static string; never NULL). */
+const char* fp8w8a8_status_string(int status);
+
+/*
+ * fp8_quant_rows - dynamic per-token quantisation (HunyuanVideo1.5 retrospective,
+ * section 3.1, second step of the chain; section 3.4 quantises one activation
+ * once and hands it to several projections).
+ *
+ *   x_bf16    device, bf16 [rows, cols], 16-byte aligned
+ *   rows      0 <= rows < FP8W8A8_MAX_ROWS (0 is a no-op)
+ *   cols      16 <= cols <= FP8W8A8_MAX_DIM, cols % 16 == 0
+ *   q_out     device, u8 e4m3fn codes [rows, cols], 16-byte aligned, written
+ *   scale_out device, fp32 [rows], 4-byte aligned, written: s[r] = fl32(amax_r / 448)
+ *   stream    hipStream_t or NULL
+ * Inputs must be finite (NaN / Inf give unspecified codes). Codes and scales are
+ * bit-identical to the definition at the top of this file.
+ */
+int fp8_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, void* q_out, float* scale_out,
+                   void* stream);
+
+/*
+ * fp8_quant_weights_per_channel - quantise an nn.Linear weight W [n, k] per output
+ * channel, ahead of time (retrospective, section 2: weights are quantised per
+ * channel in advance). Same arithmetic and arguments as fp8_quant_rows with
+ * rows = n, cols = k; n == 0 or k == 0 is FP8W8A8_ERR_BAD_SHAPE.
+ */
+int fp8_quant_weights_per_channel(const void* w_bf16, int64_t n, int64_t k, void* w_fp8_out,
+                                  float* w_scale_out, void* stream);
+
+/*
+ * A constructed linear: validated shapes, borrowed weight pointers and the GEMM
+ * kernel configuration chosen for each activation-row bucket. The choice is made
+ * once here from (n, k, bias present, compute-unit count), as the retrospective's
+ * section 3.3 asks (bind the backend at construction, keep the forward narrow),
+ * and per call only one integer compare on m picks the bucket (section 3.2: FFN-up
+ * and FFN-down shapes want different tiles).
+ */
+typedef struct fp8_linear_plan fp8_linear_plan;
+
+/*
+ * fp8_linear_create - build a plan for out[m, n] = A[m, k] x W[n, k]^T.
+ *
+ *   device     HIP device ordinal; must be a gfx950 GPU (else FP8W8A8_ERR_BAD_DEVICE)
+ *   n, k       16 <= n, k <= FP8W8A8_MAX_DIM, both multiples of 16
+ *   w_fp8      device, e4m3fn codes [n, k], 16-byte aligned (borrowed)
+ *   w_scale    device, fp32 [n], 16-byte aligned (borrowed)
+ *   bias_bf16  device, bf16 [n], 16-byte aligned, or NULL for no bias (borrowed)
+ *   out        receives the plan; unchanged on error
+ * Shape, pointer and alignment checks run before the device is queried.
+ */
+int fp8_linear_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+                      const void* bias_bf16, fp8_linear_plan** out);
+
+/*
+ * Workspace a FP8W8A8_A_BF16 run with m rows needs: the per-token codes [m, k]
+ * then the scales [m], each rounded up to 256 bytes. 0 for m <= 0 and for a NULL plan.
+ * FP8W8A8_A_E4M3 runs need no workspace.
+ */
+size_t fp8_linear_workspace_bytes(const fp8_linear_plan* plan, int64_t m);
+
+/*
+ * fp8_linear_run - one forward of the linear (retrospective, section 3.3: a plain
+ * tensor is quantised and multiplied; an FP8 tensor goes straight to the GEMM;
+ * section 3.5: an input that is already e4m3fn comes with its per-token scale).
+ *
+ *   plan        from fp8_linear_create
+ *   m           0 <= m < FP8W8A8_MAX_ROWS (0 is a no-op)
+ *   a           device; bf16 [m, k] (a_kind FP8W8A8_A_BF16) or e4m3fn codes [m, k]
+ *               (FP8W8A8_A_E4M3); 16-byte aligned
+ *   a_kind      FP8W8A8_A_BF16 or FP8W8A8_A_E4M3
+ *   a_scale     device fp32 [m], 4-byte aligned: required for FP8W8A8_A_E4M3, ignored
+ *               (may be NULL) for FP8W8A8_A_BF16
+ *   out_bf16    device, bf16 [m, n], 16-byte aligned, written
+ *   workspace   device, 256-byte aligned, at least fp8_linear_workspace_bytes(plan, m)
+ *               bytes for FP8W8A8_A_BF16 (after the call it holds qA then s);
+ *               ignored for FP8W8A8_A_E4M3
+ *   stream      hipStream_t or NULL; the quantisation and the GEMM are two launches
+ *               on this stream, in order, with no synchronisation
+ */
+int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind,
+                   const float* a_scale, void* out_bf16, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Free a plan (NULL is ignored). Does not touch the borrowed device buffers. */
+void fp8_linear_destroy(fp8_linear_plan* plan);
+
+/*
+ * fp8_linear - one-shot create + run + destroy with the same arguments and rules
+ * as those calls (device = the current HIP device). Convenience for tests and
+ * scripts; a model keeps a plan instead, so the forward does no set-up work.
+ */
+int fp8_linear(const void* a, int a_kind, const float* a_scale, int64_t m, int64_t n, int64_t k,
+               const void* w_fp8, const float* w_scale, const void* bias_bf16, void* out_bf16,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Introspection of the construction-time choice (for tests and reports).
+ * fp8_linear_plan_config writes, for an activation with m rows, the id of the GEMM
+ * kernel configuration the plan launches and its tile (block rows in m, block
+ * columns in n), and the number of workgroups. Returns FP8W8A8_ERR_INVALID_ARG for
+ * a NULL plan or output pointer.
+ */
+int fp8_linear_plan_config(const fp8_linear_plan* plan, int64_t m, int* config_id, int* tile_m,
+                           int* tile_n, int64_t* workgroups);
+
+/* Number of GEMM kernel configurations compiled in (ids 0 .. count-1). */
+int fp8_gemm_config_count(void);
+
+/*
+ * fp8_gemm_run_config - launch one named GEMM kernel configuration directly on
+ * already-quantised operands, bypassing the selector: out = epilogue(qA x qW^T).
+ * It exists so that tests can hold every compiled configuration to the same
+ * parity bar; arguments follow fp8_linear_create / fp8_linear_run (E4M3 kind),
+ * config_id must be in [0, fp8_gemm_config_count()).
+ */
+int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* qa,
+                        const float* a_scale, const void* w_fp8, const float* w_scale,
+                        const void* bias_bf16, void* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W8A8_H */

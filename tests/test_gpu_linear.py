@@ -1,0 +1,202 @@
+"""GPU parity of the FP8 W8A8 linear against the float64 CPU oracle.
+
+Every GPU output is compared with the oracle's unrounded reference computed from
+the same bf16 inputs (the oracle quantises them itself): elementwise
+|gpu - ref| <= 1e-2 (|ref| + 1) and relative Frobenius error <= 2e-3. Quantised
+activations and weights are compared bit for bit on the way. Covered: the tiny
+config in full; every compiled GEMM configuration on ragged m / n / k tails; the
+selector's plans at the four full-size workloads on sampled rows; the e4m3fn
+pass-through input; A = 0 (output == bias exactly); no bias; guard bands.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_quantized_token_amd as fp8
+from fp8_w8a8_quantized_token_amd import Fp8Linear, gemm_config_count, gemm_run_config, quant_rows
+from oracle import e4m3, linear as ol, quant as oq
+from tests._helpers import assert_linear_close, bf16_out_to_f64, require_gpu, sample_rows
+from workloads import bf16_bits, make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_weight(w_cpu):
+    return oq.quant_weights_per_channel(bf16_bits(w_cpu))
+
+
+def _bias_bits(b):
+    return None if b is None else bf16_bits(b)
+
+
+def test_tiny_config_full():
+    dev = require_gpu()
+    cfg = make_config("tiny")
+    a, w, b = cfg["activations"]["a"], cfg["weights"]["linear"], cfg["biases"]["linear"]
+    lin = Fp8Linear(w.to(dev), b.to(dev))
+    out = lin(a.to(dev))
+    qa, sa = quant_rows(a.to(dev))
+    torch.cuda.synchronize()
+    qw, sw = _oracle_weight(w)
+    assert np.array_equal(lin.w_fp8.cpu().numpy(), qw) and np.array_equal(lin.w_scale.cpu().numpy(), sw)
+    ref, eqa, esa = ol.linear_ref(bf16_bits(a), qw, sw, bf16_bits(b))
+    assert np.array_equal(qa.cpu().numpy(), eqa) and np.array_equal(sa.cpu().numpy(), esa)
+    assert_linear_close(out, ref, "tiny")
+
+
+TAIL_SHAPES = [(1, 16, 16), (26, 144, 48), (63, 16, 272), (65, 144, 16), (257, 144, 272), (300, 272, 400),
+               (513, 528, 1040)]
+
+
+@pytest.mark.parametrize("config", range(5))
+@pytest.mark.parametrize("m,n,k", TAIL_SHAPES)
+def test_every_config_on_ragged_tails(config, m, n, k):
+    dev = require_gpu()
+    assert config < gemm_config_count()
+    case = make_case(m, n, k, seed=m + n + k, kind="outlier")
+    qa, sa = oq.quant_rows(bf16_bits(case.a))
+    qw, sw = _oracle_weight(case.w)
+    ref = ol.linear_ref_fp8(qa, sa, qw, sw, _bias_bits(case.bias))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    out = gemm_run_config(config, t(qa), t(sa), t(qw), t(sw), case.bias.to(dev))
+    torch.cuda.synchronize()
+    assert_linear_close(out, ref, f"config {config} {m}x{n}x{k}")
+
+
+def test_zero_activation_gives_bias_exactly():
+    dev = require_gpu()
+    case = make_case(70, 272, 256, seed=3)
+    lin = Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    out = lin(torch.zeros((70, 256), dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    expect = case.bias.expand(70, 272)
+    assert torch.equal(out.cpu(), expect)
+
+
+def test_no_bias_and_gelu_input():
+    dev = require_gpu()
+    case = make_case(200, 160, 512, seed=4, kind="gelu", with_bias=False)
+    lin = Fp8Linear(case.w.to(dev))
+    out = lin(case.a.to(dev))
+    torch.cuda.synchronize()
+    qw, sw = _oracle_weight(case.w)
+    ref, _, _ = ol.linear_ref(bf16_bits(case.a), qw, sw, None)
+    assert_linear_close(out, ref, "no bias")
+
+
+def test_fp8_input_passthrough_matches_bf16_path():
+    dev = require_gpu()
+    case = make_case(333, 384, 1024, seed=6)
+    lin = Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    a = case.a.to(dev)
+    out_bf16 = lin(a)
+    qa, sa = quant_rows(a)
+    out_fp8 = lin(qa.view(torch.float8_e4m3fn), sa)
+    out_u8 = lin(qa, sa)
+    torch.cuda.synchronize()
+    assert torch.equal(out_bf16, out_fp8) and torch.equal(out_bf16, out_u8)
+
+
+def test_three_dim_input_and_out_buffer_guard_band():
+    dev = require_gpu()
+    case = make_case(2 * 75, 144, 256, seed=8)
+    lin = Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    m, n = 150, 144
+    pad = 1024
+    buf = torch.full((pad + m * n + pad,), 12345.0, dtype=torch.bfloat16, device=dev)
+    out = buf[pad:pad + m * n]
+    res = lin(case.a.reshape(2, 75, 256).to(dev), out=out)
+    torch.cuda.synchronize()
+    assert res.shape == (2, 75, 144)
+    b = buf.cpu()
+    assert torch.all(b[:pad] == 12345.0) and torch.all(b[pad + m * n:] == 12345.0)
+    qw, sw = _oracle_weight(case.w)
+    ref, _, _ = ol.linear_ref(bf16_bits(case.a), qw, sw, bf16_bits(case.bias))
+    assert_linear_close(out.reshape(m, n), ref, "3-d input")
+
+
+def _full_size_linear(a_cpu, w_cpu, b_cpu, dev, label, rows=None, qa_gpu=None, sa_gpu=None, lin=None):
+    """Run the plan at full size on the GPU, check sampled rows against the oracle."""
+    if lin is None:
+        lin = Fp8Linear(w_cpu.to(dev), b_cpu.to(dev))
+    if qa_gpu is None:
+        out = lin(a_cpu.to(dev))
+    else:
+        out = lin(qa_gpu, sa_gpu)
+    torch.cuda.synchronize()
+    m = a_cpu.shape[0]
+    rows = sample_rows(m) if rows is None else rows
+    qw, sw = _oracle_weight(w_cpu)
+    assert np.array_equal(lin.w_fp8.cpu().numpy(), qw), f"{label}: weight codes differ"
+    ref, _, _ = ol.linear_ref(bf16_bits(a_cpu)[rows], qw, sw, bf16_bits(b_cpu))
+    got = bf16_out_to_f64(out[torch.from_numpy(rows).to(dev)])
+    return assert_linear_close(got, ref, label)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("config", ["ffn_up", "ffn_down"])
+def test_ffn_full_size(config):
+    dev = require_gpu()
+    cfg = make_config(config)
+    layer, act = cfg["layers"][0]
+    _full_size_linear(cfg["activations"][act], cfg["weights"][layer], cfg["biases"][layer], dev, config)
+
+
+@pytest.mark.slow
+def test_qkv_shared_quantisation_full_size():
+    dev = require_gpu()
+    cfg = make_config("qkv")
+    hidden, enc = cfg["activations"]["hidden"], cfg["activations"]["encoder"]
+    qh, sh = quant_rows(hidden.to(dev))  # quantised once, fed to all three projections
+    qe, se = quant_rows(enc.to(dev))
+    for layer in ("q", "k", "v"):
+        w, b = cfg["weights"][layer], cfg["biases"][layer]
+        lin = Fp8Linear(w.to(dev), b.to(dev))
+        _full_size_linear(hidden, w, b, dev, f"qkv/{layer}", qa_gpu=qh, sa_gpu=sh, lin=lin)
+        _full_size_linear(enc, w, b, dev, f"qkv/{layer}_enc", rows=np.arange(26), qa_gpu=qe, sa_gpu=se, lin=lin)
+
+
+@pytest.mark.slow
+def test_dit_block_full_size():
+    dev = require_gpu()
+    cfg = make_config("dit_block")
+    quantised = {}
+    for name, a in cfg["activations"].items():
+        quantised[name] = quant_rows(a.to(dev))
+    for layer, act in cfg["layers"]:
+        w, b = cfg["weights"][layer], cfg["biases"][layer]
+        qa, sa = quantised[act]
+        _full_size_linear(cfg["activations"][act], w, b, dev, f"dit/{layer}", qa_gpu=qa, sa_gpu=sa,
+                          rows=sample_rows(cfg["activations"][act].shape[0], count=96))
+
+
+def test_selector_is_fixed_at_construction():
+    dev = require_gpu()
+    w = torch.zeros((2048, 8192), dtype=torch.bfloat16, device=dev)
+    lin = Fp8Linear(w)
+    seen = {m: lin.config(m) for m in (1, 26, 64, 65, 4096, 32760)}
+    for m, (cid, tm, tn, wg) in seen.items():
+        assert 0 <= cid < gemm_config_count()
+        assert wg == ((m + tm - 1) // tm) * ((2048 + tn - 1) // tn)
+        assert lin.config(m) == (cid, tm, tn, wg)  # same answer every call
+
+
+def test_errors_are_statuses_not_crashes():
+    dev = require_gpu()
+    w = torch.zeros((32, 64), dtype=torch.bfloat16, device=dev)
+    lin = Fp8Linear(w)
+    with pytest.raises(ValueError):
+        lin(torch.zeros((4, 48), dtype=torch.bfloat16, device=dev))
+    from fp8_w8a8_quantized_token_amd import _lib
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((4, 32), dtype=torch.bfloat16, device=dev)
+    st = _lib.lib().fp8_linear_run(lin._plan, 4, ctypes.c_void_p(a.data_ptr()), _lib.A_BF16, None,
+                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), 16, None)
+    assert st == _lib.ERR_WORKSPACE_TOO_SMALL
+    st = _lib.lib().fp8_linear_run(lin._plan, 4, ctypes.c_void_p(a.data_ptr()), _lib.A_E4M3, None,
+                                   ctypes.c_void_p(out.data_ptr()), None, 0, None)
+    assert st == _lib.ERR_INVALID_ARG
