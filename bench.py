@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run 3 plain 1 GiB device-to-device copies (a known-size kernel "
+                         "for scaling HBM counter readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -225,6 +228,13 @@ def main():
         },
         "gemm_median_us": round(gemm_ms[len(gemm_ms) // 2] * 1e3, 3),
     }
+    if args.copy_calibration:
+        src = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

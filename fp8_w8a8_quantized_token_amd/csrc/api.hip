@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "internal.h"
@@ -32,7 +33,6 @@ struct fp8_linear_plan {
 
 namespace {
 
-constexpr int64_t kMaxWorkgroupThreads = 256;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -79,11 +79,13 @@ int check_weight_args(int64_t n, int64_t k, const void* w, const float* w_scale,
 }
 
 bool grid_fits(int config, int64_t m, int64_t n) {
-  return gemm_workgroups(config, m, n) * kMaxWorkgroupThreads < kMaxGridThreads;
+  return gemm_workgroups(config, m, n) * gemm_threads(config) < kMaxGridThreads;
 }
 
 // Relative throughput of one workgroup of each configuration when it has a CU to
-// itself, and how many of its workgroups share a CU (LDS / register bound).
+// itself, and how many of its workgroups share a CU (LDS / register bound). Measured
+// on MI355X: the 256 x 256 tiles run at the highest per-CU rate, 256 x 128 and
+// 128 x 256 close to it, the 4-wave 128 x 128 and 64 x 64 tiles well below.
 struct TileModel {
   double eff;
   int per_cu;
@@ -91,22 +93,23 @@ struct TileModel {
 TileModel tile_model(int config) {
   switch (config) {
     case 0: return {1.00, 1};
-    case 1: return {0.92, 1};
-    case 2: return {0.92, 1};
-    case 3: return {0.80, 2};
-    default: return {0.45, 4};
+    case 1: return {0.99, 1};
+    case 2: return {0.95, 1};
+    case 3: return {0.96, 1};
+    case 4: return {0.80, 2};
+    default: return {0.40, 4};
   }
 }
 
-// Estimated time (arbitrary units) of configuration c on an m x n output.
+// Estimated time (arbitrary units) of configuration c on an m x n output: rounds of
+// co-resident tiles times the work of one round.
 double model_time(int c, int64_t m, int64_t n, int cus) {
   const GemmConfig* g = gemm_config(c);
   const TileModel t = tile_model(c);
   const int64_t tiles = gemm_workgroups(c, m, n);
-  const int64_t slots = (int64_t)cus * t.per_cu;
-  const int64_t waves = (tiles + slots - 1) / slots;
-  // a wave of `per_cu` co-resident tiles costs per_cu tiles' work at the tile's efficiency
-  return (double)waves * t.per_cu * (double)g->tile_m * (double)g->tile_n / t.eff;
+  const int64_t conc = std::min<int64_t>(t.per_cu, (tiles + cus - 1) / cus);
+  const int64_t rounds = (tiles + cus * conc - 1) / (cus * conc);
+  return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n / t.eff;
 }
 
 int choose_config(int64_t m, int64_t n, int cus) {

@@ -3,37 +3,48 @@
 //   out[m, n] = bf16_rne( acc[m, n] * a_scale[m] * w_scale[n] + bias[n] ),
 //   acc[m, n] = sum_k dec(qa[m, k]) * dec(qw[n, k])   (fp32 accumulation on the MFMA units)
 //
-// This is the "FP8 GEMM" and "scale / bias / output dtype" part of the chain in
-// the HunyuanVideo1.5 BF16->FP8 retrospective (aigcage.com, section 3.1). Both
-// operands are k-contiguous: the activation codes [m, k] and the weight in
-// nn.Linear's [n, k] layout (the page's column-major B, never transposed).
-// Section 3.2 of the page finds that tile shape and the full epilogue, not the
-// bare GEMM, decide the speed; the design here is gfx950's own:
+// This is the "FP8 GEMM" and "scale / bias / output dtype" part of the chain in the
+// HunyuanVideo1.5 BF16->FP8 retrospective (aigcage.com, section 3.1). Both operands
+// are k-contiguous: the activation codes [m, k] and the weight in nn.Linear's [n, k]
+// layout (the page's column-major B, never transposed). Section 3.2 of the page finds
+// that the tile shape, the memory pipeline and the full epilogue, not the bare GEMM,
+// decide the speed. The design here is gfx950's own:
 //
-//   * V_MFMA_F32_16X16X128_F8F6F4: the weight rows feed the MFMA's first operand
-//     and the activation rows its second, so each lane's four fp32 results are
-//     four consecutive output channels of one token and leave as one 8-byte store;
-//   * block tiles of BM (tokens) x BN (channels) x 128 bytes of k, double-buffered
-//     in LDS and filled by buffer_load_dwordx4 ... lds (global -> LDS with no VGPR
-//     staging). The buffer descriptor covers only the valid rows of the block and
-//     lanes past k are pointed out of range, so ragged m / n / k tails read zeros
-//     and never touch memory outside the operands;
-//   * a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) makes both the LDS fill and
-//     the ds_read_b128 operand reads bank-conflict free;
-//   * workgroup ids are remapped so each of the 8 XCDs (own L2 each) walks a
-//     contiguous, m-grouped range of tiles, keeping shared operand panels in one L2.
+//   * V_MFMA_F32_32X32X64_F8F6F4. The weight rows feed the MFMA's first operand and
+//     the activation rows its second, so a lane's results come in runs of four
+//     consecutive output channels of one token: one 8-byte bf16 store each.
+//   * Block tiles of BM tokens x BN channels, 64 bytes of k per stage, STAGES stage
+//     buffers in LDS (up to the 160 KiB of a CU). Stages are filled by
+//     buffer_load_dwordx4 ... lds (HBM/L2 -> LDS with no VGPR staging) STAGES - 1
+//     sub-steps ahead of their use, so an L2 miss has several MFMA sub-steps to land.
+//     Each wave waits with a precise vmcnt for its own fills of the stage it is about
+//     to read, then the workgroup barrier publishes every wave's fills.
+//   * The buffer descriptors cover only the block's valid rows, and lanes past k are
+//     pointed out of range: ragged m / n / k tails read zeros and no access leaves
+//     the operands.
+//   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at position
+//     c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), which makes the fills and the
+//     ds_read_b128 operand reads free of bank conflicts.
+//   * Two waves per SIMD (8-wave workgroups) for the large tiles, so one wave's
+//     barrier or LDS wait is covered by the other's MFMAs.
+//   * Workgroup ids are remapped so each of the 8 XCDs (own L2 each) walks a
+//     contiguous, m-grouped range of tiles and concurrent tiles share panels in L2.
+//   * The tile's scales and bias are requested at kernel start (one value per
+//     thread), staged through LDS after the k loop, and applied in fp32 with a single
+//     rounding to bf16.
 #include "internal.h"
 
 namespace fp8w8a8 {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 128;          // k bytes per stage (one MFMA k-step)
+constexpr int kBK = 64;           // k bytes per stage (one 32x32x64 MFMA k-step)
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: dword3 data format
+constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer descriptor, word 3
 
 struct GemmArgs {
   const uint8_t* qa;
@@ -46,24 +57,36 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferConfig);
+// Raw buffer descriptor in SGPRs: 48-bit base, stride 0, num_records bytes.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kBufferConfig;
+  return r;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_ptr_t dst, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, 0);
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes land at LDS address lds + 16 i. Issued
+// from inline asm so the compiler does not make every later LDS read wait for all
+// fills in flight; the kernel waits for exactly the fills it needs (vmcnt) and
+// synchronises the workgroup itself. The instruction has no register result.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // v_cvt_pk_bf16_f32: round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin
-// (id % 8); renumber so XCD x owns a contiguous range of logical tiles, then walk
-// that range in groups of GROUP_M tile rows so concurrent tiles share panels.
+// Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin (id % 8);
+// renumber so XCD x owns a contiguous range of logical tiles, then walk that range in
+// groups of GROUP_M tile rows so concurrent tiles share operand panels in L2.
 template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nwg = gridDim.x;
@@ -80,150 +103,245 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int GROUP_M>
+// Distinct LDS objects per (kernel, stage).
+template <typename Tag, int I, int BYTES>
+__device__ __forceinline__ uint8_t* stage_buf() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
+  return buf;
+}
+
+// s_waitcnt with vmcnt = N (0..63) and lgkmcnt = 0 (gfx9 encoding, expcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Wait until the fills of the stage about to be read have landed, allowing the
+// `pending` younger stages (F fills each) to stay in flight.
+template <int F, int S>
+__device__ __forceinline__ void wait_stage(int pending) {
+  if constexpr (S >= 6) {
+    if (pending >= 4) { wait_vm_lgkm0<4 * F>(); return; }
+  }
+  if constexpr (S >= 5) {
+    if (pending >= 3) { wait_vm_lgkm0<3 * F>(); return; }
+  }
+  if constexpr (S >= 4) {
+    if (pending >= 2) { wait_vm_lgkm0<2 * F>(); return; }
+  }
+  if constexpr (S >= 3) {
+    if (pending >= 1) { wait_vm_lgkm0<F>(); return; }
+  }
+  wait_vm_lgkm0<0>();
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+struct KernelTag {};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
+  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, GROUP_M>;
+  constexpr int BK = kBK;
   constexpr int kWaves = WAVES_M * WAVES_N;
   constexpr int WTM = BM / WAVES_M;  // wave tile along m (tokens)
   constexpr int WTN = BN / WAVES_N;  // wave tile along n (channels)
-  constexpr int FM = WTM / 16;       // 16-token fragments per wave
-  constexpr int FN = WTN / 16;       // 16-channel fragments per wave
-  constexpr int kStageBytes = (BM + BN) * kBK;
-  constexpr int kRowGroups = (BM + BN) / 8;  // one wave-wide LDS fill covers 8 rows x 128 B
-  static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile / wave mismatch");
+  constexpr int FM = WTM / 32;
+  constexpr int FN = WTN / 32;
+  constexpr int kStageBytes = (BM + BN) * BK;
+  constexpr int kRowGroups = (BM + BN) / 16;  // one wave-wide fill: 16 rows x 64 B
+  static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile / wave mismatch");
   static_assert(kRowGroups % kWaves == 0, "fill work must split evenly across waves");
-  constexpr int kFillsPerWave = kRowGroups / kWaves;
+  static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS budget of a CU");
+  constexpr int F = kRowGroups / kWaves;  // fills per wave per stage
+  static_assert((STAGES - 2) * F < 64, "vmcnt range");
+  static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
+  static_assert((BM + 2 * BN) * 4 <= kStageBytes, "epilogue staging fits in one stage");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+  auto buf = [](int s) -> uint8_t* {
+    switch (s) {
+      case 0: return stage_buf<Tag, 0, kStageBytes>();
+      case 1: return stage_buf<Tag, 1, kStageBytes>();
+      case 2: return stage_buf<Tag, 2 % STAGES, kStageBytes>();
+      case 3: return stage_buf<Tag, 3 % STAGES, kStageBytes>();
+      case 4: return stage_buf<Tag, 4 % STAGES, kStageBytes>();
+      default: return stage_buf<Tag, 5 % STAGES, kStageBytes>();
+    }
+  };
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-
   int tm, tn;
   tile_coords<GROUP_M>(args.tiles_m, args.tiles_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);  // uniform by construction; keep it in SGPRs
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int m0 = tm * BM, n0 = tn * BN;
   const int K = args.k;
   const int rows_a = min(BM, args.m - m0);
   const int rows_w = min(BN, args.n - n0);
+  const v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+  const v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
-  const __amdgpu_buffer_rsrc_t rsrc_a =
-      make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rsrc_w =
-      make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  // Epilogue operands of this tile, one value per thread, requested now so their
+  // latency hides behind the k loop.
+  const int tid = threadIdx.x;
+  float pre_sa = 0.0f, pre_sw = 0.0f, pre_b = 0.0f;
+  if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
+  if (tid < BN && tid < rows_w) {
+    pre_sw = args.w_scale[n0 + tid];
+    if (args.bias) pre_b = __uint_as_float((uint32_t)args.bias[n0 + tid] << 16);
+  }
 
-  // Fill geometry: in a wave-wide fill lane i writes LDS bytes [16 i, 16 i + 16) of
-  // an 8-row group, i.e. row i/8, chunk position i%8, which holds logical chunk
-  // (i%8) ^ (i/8) of that row.
-  const int fill_row = lane >> 3;
-  const int fill_chunk = (lane & 7) ^ fill_row;
-  const uint32_t fill_off = (uint32_t)fill_row * (uint32_t)K + 16u * (uint32_t)fill_chunk;
+  // Fill geometry: a wave-wide fill covers 16 rows x 64 B = 1 KiB of a stage; lane i
+  // writes bytes [16 i, 16 i + 16): row i/4 of the group, position i%4, which holds
+  // logical chunk (i%4) ^ f(i/4). Tile rows 0..BM-1 are the activation, BM.. the weight.
+  const int fr = lane >> 2;
+  const int fchunk = (lane & 3) ^ (((fr >> 1) & 3) ^ ((fr >> 3) & 1));
+  const uint32_t foff = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk;
 
-  auto issue_stage = [&](int stage, int k0) {
-    const bool kvalid = k0 + 16 * fill_chunk < K;
-    uint8_t* base = smem + stage * kStageBytes;
+  auto issue = [&](uint8_t* base, int k0) {
+    const bool kvalid = k0 + 16 * fchunk < K;
 #pragma unroll
-    for (int j = 0; j < kFillsPerWave; ++j) {
-      const int g = wave + j * kWaves;  // row group
-      lds_ptr_t dst = (lds_ptr_t)(base + g * 1024);
-      if (g * 8 < BM) {
-        const uint32_t vo = kvalid ? (uint32_t)(g * 8) * (uint32_t)K + fill_off + (uint32_t)k0 : kOutOfRange;
-        load_lds16(rsrc_a, dst, vo);
+    for (int j = 0; j < F; ++j) {
+      const int g = wave + j * kWaves;
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
+      if (g * 16 < BM) {
+        const uint32_t vo = kvalid ? (uint32_t)(g * 16) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        dma16(rsrc_a, dst, vo);
       } else {
-        const uint32_t vo =
-            kvalid ? (uint32_t)(g * 8 - BM) * (uint32_t)K + fill_off + (uint32_t)k0 : kOutOfRange;
-        load_lds16(rsrc_w, dst, vo);
+        const uint32_t vo = kvalid ? (uint32_t)(g * 16 - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        dma16(rsrc_w, dst, vo);
       }
     }
   };
 
-  // Operand reads: lane l reads row (l % 16) of a 16-row fragment, k bytes
-  // [32 (l/16), +32) = logical chunks 2 (l/16) and 2 (l/16) + 1, swizzled by row & 7 = l & 7.
-  const int frag_row = lane & 15;
-  const int kq = lane >> 4;
-  const int sw = lane & 7;
-  const uint32_t rd0 = (uint32_t)frag_row * kBK + 16u * (uint32_t)((2 * kq) ^ sw);
-  const uint32_t rd1 = (uint32_t)frag_row * kBK + 16u * (uint32_t)((2 * kq + 1) ^ sw);
+  // Operand reads for the 32x32x64 MFMA: lane l holds row l % 32 of a 32-row
+  // fragment, k bytes [32 (l/32), +32) = logical chunks 2 (l/32) and 2 (l/32) + 1.
+  const int rrow = lane & 31;
+  const int rkq = lane >> 5;
+  const int rf = ((rrow >> 1) & 3) ^ ((rrow >> 3) & 1);
+  const uint32_t rd0 = (uint32_t)rrow * BK + 16u * (uint32_t)((2 * rkq) ^ rf);
+  const uint32_t rd1 = (uint32_t)rrow * BK + 16u * (uint32_t)((2 * rkq + 1) ^ rf);
 
-  v4f acc[FN][FM];
+  v16f acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int ktiles = (K + kBK - 1) / kBK;
-  issue_stage(0, 0);
-  for (int kt = 0; kt < ktiles; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < ktiles) issue_stage((kt + 1) & 1, (kt + 1) * kBK);
-
-    const uint8_t* sa = smem + (kt & 1) * kStageBytes + (wm * WTM) * kBK;
-    const uint8_t* sw_ = smem + (kt & 1) * kStageBytes + (BM + wn * WTN) * kBK;
-    v8i afrag[FM];
+  auto compute = [&](const uint8_t* base) {
+    const uint8_t* sa = base + (wm * WTM) * BK;
+    const uint8_t* sw = base + (BM + wn * WTN) * BK;
+    v8i af[FM];
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sa + j * 16 * kBK + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sa + j * 16 * kBK + rd1);
-      afrag[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint4 lo = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd1);
+      af[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sw_ + i * 16 * kBK + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sw_ + i * 16 * kBK + rd1);
-      const v8i wfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint4 lo = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd1);
+      const v8i wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfrag, afrag[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  };
+
+  // k loop, unrolled by STAGES so every stage buffer is a compile-time object.
+  // Sub-step t: wait for stage t (its younger stages stay in flight), barrier (all
+  // waves' fills of t landed; all waves done reading stage t-1), refill the buffer of
+  // stage t-1 with stage t + STAGES - 1, multiply stage t.
+  const int nks = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nks) issue(buf(s), s * BK);
+  for (int ks0 = 0; ks0 < nks; ks0 += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      const int t = ks0 + s;
+      if (t < nks) {
+        wait_stage<F, STAGES>(min(nks - 1 - t, STAGES - 2));
+        block_barrier();
+        if (t + STAGES - 1 < nks) issue(buf((s + STAGES - 1) % STAGES), (t + STAGES - 1) * BK);
+        compute(buf(s));
+      }
     }
   }
 
-  // Epilogue: lane holds, for fragment (i, j), channels n = .. + 4 (l/16) + 0..3 of token
-  // m = .. + (l % 16). One fp32 expression, one rounding to bf16, one 8-byte store.
+  // Stage the epilogue operands in LDS (stage buffer 0 is free once every wave has
+  // finished its last operand reads).
+  float* epi_sa = reinterpret_cast<float*>(buf(0));
+  float* epi_sw = epi_sa + BM;
+  float* epi_b = epi_sw + BN;
+  block_barrier();
+  if (tid < BM) epi_sa[tid] = pre_sa;
+  if (tid < BN) {
+    epi_sw[tid] = pre_sw;
+    epi_b[tid] = pre_b;
+  }
+  wait_vm_lgkm0<63>();  // lgkmcnt(0): the LDS writes are done
+  block_barrier();
+
+  // Epilogue: for fragment (i, j) lane l holds token m = .. + l % 32 and, for q = 0..3,
+  // channels n = .. + 8 q + 4 (l/32) + 0..3 (registers 4 q .. 4 q + 3). One fp32
+  // expression, one rounding to bf16, one 8-byte store per 4 channels.
   const int64_t N = args.n;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int m = m0 + wm * WTM + j * 16 + (lane & 15);
-    if (m >= args.m) continue;
-    const float sa = args.a_scale[m];
+    const int ml = wm * WTM + j * 32 + (lane & 31);
+    const int m = m0 + ml;
+    const float sa = epi_sa[ml];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const int n = n0 + wn * WTN + i * 16 + 4 * (lane >> 4);
-      if (n >= args.n) continue;
-      const float4 sw4 = *reinterpret_cast<const float4*>(args.w_scale + n);
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
-      if (args.bias) {
-        const uint2 braw = *reinterpret_cast<const uint2*>(args.bias + n);
-        b[0] = __uint_as_float(braw.x << 16);
-        b[1] = __uint_as_float(braw.x & 0xffff0000u);
-        b[2] = __uint_as_float(braw.y << 16);
-        b[3] = __uint_as_float(braw.y & 0xffff0000u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
+        const float4 sw4 = *reinterpret_cast<const float4*>(epi_sw + nl);
+        const float4 b4 = *reinterpret_cast<const float4*>(epi_b + nl);
+        const v16f& a = acc[i][j];
+        const float o0 = __builtin_fmaf(a[4 * q + 0] * sa, sw4.x, b4.x);
+        const float o1 = __builtin_fmaf(a[4 * q + 1] * sa, sw4.y, b4.y);
+        const float o2 = __builtin_fmaf(a[4 * q + 2] * sa, sw4.z, b4.z);
+        const float o3 = __builtin_fmaf(a[4 * q + 3] * sa, sw4.w, b4.w);
+        if (m < args.m && n0 + nl < args.n)
+          *reinterpret_cast<uint2*>(args.out + (int64_t)m * N + n0 + nl) =
+              make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
       }
-      const v4f a = acc[i][j];
-      const float o0 = __builtin_fmaf(a[0] * sa, sw4.x, b[0]);
-      const float o1 = __builtin_fmaf(a[1] * sa, sw4.y, b[1]);
-      const float o2 = __builtin_fmaf(a[2] * sa, sw4.z, b[2]);
-      const float o3 = __builtin_fmaf(a[3] * sa, sw4.w, b[3]);
-      *reinterpret_cast<uint2*>(args.out + (int64_t)m * N + n) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int GM>
+template <int BM, int BN, int WM, int WN, int S, int GM>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
   const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_kernel<BM, BN, WM, WN, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+  gemm_fp8_kernel<BM, BN, WM, WN, S, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
+// id, tile_m, tile_n, waves, stages, name
 const GemmConfig kConfigs[] = {
-    {0, 256, 256, "bm256_bn256_w2x2"},
-    {1, 256, 128, "bm256_bn128_w2x2"},
-    {2, 128, 256, "bm128_bn256_w2x2"},
-    {3, 128, 128, "bm128_bn128_w2x2"},
-    {4, 64, 64, "bm64_bn64_w2x2"},
+    {0, 256, 256, 8, 4, "bm256_bn256_w4x2_s4"},
+    {1, 256, 256, 8, 5, "bm256_bn256_w2x4_s5"},
+    {2, 256, 128, 8, 6, "bm256_bn128_w4x2_s6"},
+    {3, 128, 256, 8, 6, "bm128_bn256_w2x4_s6"},
+    {4, 128, 128, 4, 4, "bm128_bn128_w2x2_s4"},
+    {5, 64, 64, 4, 4, "bm64_bn64_w2x2_s4"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -239,16 +357,22 @@ int64_t gemm_workgroups(int id, int64_t m, int64_t n) {
   return ((m + c->tile_m - 1) / c->tile_m) * ((n + c->tile_n - 1) / c->tile_n);
 }
 
+int gemm_threads(int id) {
+  const GemmConfig* c = gemm_config(id);
+  return c ? c->waves * 64 : 0;
+}
+
 hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* qa, const float* a_scale,
                        const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
                        hipStream_t stream) {
   GemmArgs a{qa, a_scale, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
   switch (id) {
-    case 0: return launch<256, 256, 2, 2, 4>(a, stream);
-    case 1: return launch<256, 128, 2, 2, 4>(a, stream);
-    case 2: return launch<128, 256, 2, 2, 4>(a, stream);
-    case 3: return launch<128, 128, 2, 2, 8>(a, stream);
-    case 4: return launch<64, 64, 2, 2, 8>(a, stream);
+    case 0: return launch<256, 256, 4, 2, 4, 4>(a, stream);
+    case 1: return launch<256, 256, 2, 4, 5, 4>(a, stream);
+    case 2: return launch<256, 128, 4, 2, 6, 4>(a, stream);
+    case 3: return launch<128, 256, 2, 4, 6, 4>(a, stream);
+    case 4: return launch<128, 128, 2, 2, 4, 8>(a, stream);
+    case 5: return launch<64, 64, 2, 2, 4, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -18,14 +18,17 @@ struct GemmConfig {
   int id;
   int tile_m;   // block rows along m (activation rows)
   int tile_n;   // block columns along n (weight rows / output channels)
+  int waves;    // 64-lane wavefronts per workgroup
+  int stages;   // LDS pipeline depth (64 bytes of k per stage)
   const char* name;
 };
 
 int gemm_config_count();
 const GemmConfig* gemm_config(int id);
 
-// Workgroups a configuration launches for an m x n output.
+// Workgroups a configuration launches for an m x n output, and threads per workgroup.
 int64_t gemm_workgroups(int id, int64_t m, int64_t n);
+int gemm_threads(int id);
 
 // Launch configuration `id` for out[m, n] = epilogue(qa[m, k] x qw[n, k]^T).
 hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* qa, const float* a_scale,

@@ -51,7 +51,7 @@ TAIL_SHAPES = [(1, 16, 16), (26, 144, 48), (63, 16, 272), (65, 144, 16), (257, 1
                (513, 528, 1040)]
 
 
-@pytest.mark.parametrize("config", range(5))
+@pytest.mark.parametrize("config", range(6))
 @pytest.mark.parametrize("m,n,k", TAIL_SHAPES)
 def test_every_config_on_ragged_tails(config, m, n, k):
     dev = require_gpu()
