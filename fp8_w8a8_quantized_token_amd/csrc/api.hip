@@ -93,11 +93,10 @@ struct TileModel {
 TileModel tile_model(int config) {
   switch (config) {
     case 0: return {1.00, 1};
-    case 1: return {0.99, 1};
-    case 2: return {0.95, 1};
-    case 3: return {0.96, 1};
-    case 4: return {0.80, 2};
-    default: return {0.40, 4};
+    case 1: return {0.96, 1};
+    case 2: return {0.96, 1};
+    case 3: return {0.75, 2};
+    default: return {0.40, 3};
   }
 }
 

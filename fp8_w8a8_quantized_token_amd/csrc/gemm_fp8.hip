@@ -31,7 +31,9 @@
 //     contiguous, m-grouped range of tiles and concurrent tiles share panels in L2.
 //   * The tile's scales and bias are requested at kernel start (one value per
 //     thread), staged through LDS after the k loop, and applied in fp32 with a single
-//     rounding to bf16.
+//     rounding to bf16. The bf16 tile is then staged through LDS as well, so the
+//     output leaves in whole 128-byte lines (16 bytes per lane) instead of scattered
+//     8-byte pieces.
 #include "internal.h"
 
 namespace fp8w8a8 {
@@ -41,7 +43,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;           // k bytes per stage (one 32x32x64 MFMA k-step)
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer descriptor, word 3
@@ -118,22 +119,36 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // Wait until the fills of the stage about to be read have landed, allowing the
-// `pending` younger stages (F fills each) to stay in flight.
+// `pending` younger stages (F fills each) to stay in flight; also drains this wave's
+// LDS reads (lgkmcnt(0)) so the workgroup barrier that follows may recycle a buffer.
 template <int F, int S>
 __device__ __forceinline__ void wait_stage(int pending) {
   if constexpr (S >= 6) {
-    if (pending >= 4) { wait_vm_lgkm0<4 * F>(); return; }
+    if (pending >= 5) { wait_vm_lgkm0<5 * F>(); return; }
   }
   if constexpr (S >= 5) {
-    if (pending >= 3) { wait_vm_lgkm0<3 * F>(); return; }
+    if (pending >= 4) { wait_vm_lgkm0<4 * F>(); return; }
   }
   if constexpr (S >= 4) {
-    if (pending >= 2) { wait_vm_lgkm0<2 * F>(); return; }
+    if (pending >= 3) { wait_vm_lgkm0<3 * F>(); return; }
   }
   if constexpr (S >= 3) {
-    if (pending >= 1) { wait_vm_lgkm0<F>(); return; }
+    if (pending >= 2) { wait_vm_lgkm0<2 * F>(); return; }
   }
+  if (pending >= 1) { wait_vm_lgkm0<F>(); return; }
   wait_vm_lgkm0<0>();
+}
+
+// Interleave the MFMAs of the current sub-step with the LDS reads of the next one:
+// after each MFMA, up to R ds_reads (the matrix pipe keeps running while they issue).
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave_mfma_ds_read() {
+  constexpr int R = (READS + MFMAS - 1) / MFMAS;
+#pragma unroll
+  for (int i = 0; i < MFMAS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (R > 0 && (i + 1) * R <= READS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS reads
+  }
 }
 
 __device__ __forceinline__ void block_barrier() {
@@ -142,26 +157,40 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
 struct KernelTag {};
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+// LDS swizzle of 16-byte chunks within a tile row of BK bytes: chunk c of row r sits at
+// position c ^ swz(r). Chosen so that 16 consecutive rows read at one logical chunk hit
+// 16 distinct 16-byte bank groups of a 256-byte LDS line, and any 8 consecutive rows 8
+// distinct groups of a 128-byte line: the ds_read_b128 operand reads are conflict free.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
-  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, GROUP_M>;
-  constexpr int BK = kBK;
+  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M>;
+  static_assert(BK == 64 || BK == 128, "stage depth in k bytes");
+  constexpr int H = BK / 64;         // 32x32x64 MFMA k-steps per stage
+  constexpr int CPR = BK / 16;       // 16-byte chunks per tile row
+  constexpr int RPF = 64 / CPR;      // tile rows per wave-wide 1 KiB fill
   constexpr int kWaves = WAVES_M * WAVES_N;
   constexpr int WTM = BM / WAVES_M;  // wave tile along m (tokens)
   constexpr int WTN = BN / WAVES_N;  // wave tile along n (channels)
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
   constexpr int kStageBytes = (BM + BN) * BK;
-  constexpr int kRowGroups = (BM + BN) / 16;  // one wave-wide fill: 16 rows x 64 B
+  constexpr int kRowGroups = (BM + BN) / RPF;
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile / wave mismatch");
   static_assert(kRowGroups % kWaves == 0, "fill work must split evenly across waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS budget of a CU");
   constexpr int F = kRowGroups / kWaves;  // fills per wave per stage
-  static_assert((STAGES - 2) * F < 64, "vmcnt range");
+  static_assert((STAGES - 1) * F < 64, "vmcnt range");
+  static_assert((BM / RPF) % kWaves == 0, "activation fills split evenly across waves");
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
   static_assert((BM + 2 * BN) * 4 <= kStageBytes, "epilogue staging fits in one stage");
 
@@ -200,36 +229,49 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     if (args.bias) pre_b = __uint_as_float((uint32_t)args.bias[n0 + tid] << 16);
   }
 
-  // Fill geometry: a wave-wide fill covers 16 rows x 64 B = 1 KiB of a stage; lane i
-  // writes bytes [16 i, 16 i + 16): row i/4 of the group, position i%4, which holds
-  // logical chunk (i%4) ^ f(i/4). Tile rows 0..BM-1 are the activation, BM.. the weight.
-  const int fr = lane >> 2;
-  const int fchunk = (lane & 3) ^ (((fr >> 1) & 3) ^ ((fr >> 3) & 1));
-  const uint32_t foff = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk;
+  // Fill geometry: a wave-wide fill covers RPF rows x BK bytes = 1 KiB of a stage;
+  // lane i writes bytes [16 i, 16 i + 16): row i / CPR of the group, position i % CPR,
+  // which holds logical chunk (i % CPR) ^ swz(row). swz depends on row % 16, so with
+  // 8-row fills (BK = 128) the chunk differs between even and odd row groups. Tile rows
+  // 0..BM-1 are the activation, BM.. the weight; wave w fills row groups w, w + kWaves, ...
+  const int fr = lane / CPR;
+  const int fchunk0 = (lane % CPR) ^ swz<BK>(fr);            // row group with g * RPF % 16 == 0
+  const int fchunk1 = (lane % CPR) ^ swz<BK>(fr + RPF % 16);  // row group with g * RPF % 16 == 8
+  const uint32_t foff0 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0;
+  const uint32_t foff1 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1;
 
   auto issue = [&](uint8_t* base, int k0) {
-    const bool kvalid = k0 + 16 * fchunk < K;
+    const bool kvalid0 = k0 + 16 * fchunk0 < K;
+    const bool kvalid1 = k0 + 16 * fchunk1 < K;
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       const int g = wave + j * kWaves;
+      const bool odd = ((g * RPF) & 15) != 0;
+      const bool kvalid = odd ? kvalid1 : kvalid0;
+      const uint32_t foff = odd ? foff1 : foff0;
       const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
-      if (g * 16 < BM) {
-        const uint32_t vo = kvalid ? (uint32_t)(g * 16) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+      if (j < (BM / RPF) / kWaves) {
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_a, dst, vo);
       } else {
-        const uint32_t vo = kvalid ? (uint32_t)(g * 16 - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_w, dst, vo);
       }
     }
   };
 
-  // Operand reads for the 32x32x64 MFMA: lane l holds row l % 32 of a 32-row
-  // fragment, k bytes [32 (l/32), +32) = logical chunks 2 (l/32) and 2 (l/32) + 1.
+  // Operand reads for the 32x32x64 MFMA k-step h of a stage: lane l holds row l % 32 of
+  // a 32-row fragment, k bytes 64 h + [32 (l/32), +32) = logical chunks
+  // 4 h + 2 (l/32) and 4 h + 2 (l/32) + 1.
   const int rrow = lane & 31;
   const int rkq = lane >> 5;
-  const int rf = ((rrow >> 1) & 3) ^ ((rrow >> 3) & 1);
-  const uint32_t rd0 = (uint32_t)rrow * BK + 16u * (uint32_t)((2 * rkq) ^ rf);
-  const uint32_t rd1 = (uint32_t)rrow * BK + 16u * (uint32_t)((2 * rkq + 1) ^ rf);
+  const int rf = swz<BK>(rrow);
+  uint32_t rd0[H], rd1[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    rd0[h] = (uint32_t)rrow * BK + 16u * (uint32_t)((4 * h + 2 * rkq) ^ rf);
+    rd1[h] = (uint32_t)rrow * BK + 16u * (uint32_t)((4 * h + 2 * rkq + 1) ^ rf);
+  }
 
   v16f acc[FN][FM];
 #pragma unroll
@@ -239,50 +281,90 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto compute = [&](const uint8_t* base) {
+  // Operand fragments of one MFMA k-step: FM activation and FN weight fragments.
+  struct Frags {
+    v8i a[FM];
+    v8i w[FN];
+  };
+  auto read_frags = [&](const uint8_t* base, int h, Frags& f) {
     const uint8_t* sa = base + (wm * WTM) * BK;
     const uint8_t* sw = base + (BM + wn * WTN) * BK;
-    v8i af[FM];
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd1);
-      af[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint4 lo = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd0[h]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sa + j * 32 * BK + rd1[h]);
+      f.a[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd1);
-      const v8i wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      const uint4 lo = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd0[h]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sw + i * 32 * BK + rd1[h]);
+      f.w[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   };
+  auto mfma_all = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[i], f.a[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
 
-  // k loop, unrolled by STAGES so every stage buffer is a compile-time object.
-  // Sub-step t: wait for stage t (its younger stages stay in flight), barrier (all
-  // waves' fills of t landed; all waves done reading stage t-1), refill the buffer of
-  // stage t-1 with stage t + STAGES - 1, multiply stage t.
-  const int nks = (K + BK - 1) / BK;
+  // Software pipeline over MFMA k-steps u = H t + h (stage t, half h). Stage t lives in
+  // buffer t % STAGES; all STAGES buffers are in flight from the start. Sub-step u
+  // multiplies the fragments of u (already in registers) while it reads those of u + 1
+  // from LDS, interleaved instruction by instruction. Before the read crosses into
+  // stage t + 1, a wait + barrier publishes stage t + 1 and confirms every wave has
+  // finished reading stage t, whose buffer is then refilled with stage t + STAGES.
+  const int nst = (K + BK - 1) / BK;
+  const int nsub = nst * H;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nks) issue(buf(s), s * BK);
-  for (int ks0 = 0; ks0 < nks; ks0 += STAGES) {
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      const int t = ks0 + s;
-      if (t < nks) {
-        wait_stage<F, STAGES>(min(nks - 1 - t, STAGES - 2));
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nst) issue(buf(s), s * BK);
+  Frags f0, f1;
+  wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+  block_barrier();
+  read_frags(buf(0), 0, f0);
+
+  auto sub = [&](int u, int s, int h, Frags& cur, Frags& nxt) {
+    // s = stage index of u modulo STAGES, h = half of u (compile-time after unrolling)
+    const int t = u / H;
+    if (h == H - 1) {
+      if (t + 1 < nst) {
+        wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
         block_barrier();
-        if (t + STAGES - 1 < nks) issue(buf((s + STAGES - 1) % STAGES), (t + STAGES - 1) * BK);
-        compute(buf(s));
+        if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK);
       }
+      read_frags(buf((s + 1) % STAGES), 0, nxt);
+    } else {
+      read_frags(buf(s), h + 1, nxt);
+    }
+    mfma_all(cur);
+    interleave_mfma_ds_read<FM * FN, 2 * (FM + FN)>();
+  };
+  constexpr int kUnroll = 2 * STAGES * H;  // whole stage ring, even number of sub-steps
+  for (int u0 = 0; u0 < nsub; u0 += kUnroll) {
+#pragma unroll
+    for (int v = 0; v < kUnroll; v += 2) {
+      if (u0 + v < nsub) sub(u0 + v, (v / H) % STAGES, v % H, f0, f1);
+      if (u0 + v + 1 < nsub) sub(u0 + v + 1, ((v + 1) / H) % STAGES, (v + 1) % H, f1, f0);
     }
   }
 
-  // Stage the epilogue operands in LDS (stage buffer 0 is free once every wave has
-  // finished its last operand reads).
+  // Epilogue. The stage buffers are free once every wave has passed this barrier.
+  // 1. Stage the tile's scales and bias in LDS, then pull each lane's share into
+  //    registers (the operand fragments are dead by now).
+  // 2. Each wave applies them to its accumulators in fp32, rounds once to bf16 and
+  //    writes its WTM x WTN tile row-major into its own LDS region (16-byte chunk c of
+  //    row r at chunk position c ^ (r % RC)).
+  // 3. Each wave reads its region back a row segment per lane group and stores whole
+  //    rows (16 bytes per lane, full 128-byte lines) to the output.
+  constexpr int RC = WTN / 8;                     // 16-byte chunks in a wave-tile row
+  constexpr int kWaveOutBytes = WTM * WTN * 2;
+  constexpr int kWavesPerBuf = kStageBytes / kWaveOutBytes;
+  static_assert(kWavesPerBuf >= 1 && (kWaves + kWavesPerBuf - 1) / kWavesPerBuf <= STAGES,
+                "output staging fits in the stage buffers");
+  static_assert(64 % RC == 0 && (WTM * RC) % 64 == 0, "row segments tile the wavefront");
   float* epi_sa = reinterpret_cast<float*>(buf(0));
   float* epi_sw = epi_sa + BM;
   float* epi_b = epi_sw + BN;
@@ -294,54 +376,75 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   }
   wait_vm_lgkm0<63>();  // lgkmcnt(0): the LDS writes are done
   block_barrier();
+  float r_sa[FM];
+  float4 r_sw[FN][4], r_b[FN][4];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) r_sa[j] = epi_sa[wm * WTM + j * 32 + (lane & 31)];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
+      r_sw[i][q] = *reinterpret_cast<const float4*>(epi_sw + nl);
+      r_b[i][q] = *reinterpret_cast<const float4*>(epi_b + nl);
+    }
+  wait_vm_lgkm0<63>();
+  block_barrier();
 
-  // Epilogue: for fragment (i, j) lane l holds token m = .. + l % 32 and, for q = 0..3,
-  // channels n = .. + 8 q + 4 (l/32) + 0..3 (registers 4 q .. 4 q + 3). One fp32
-  // expression, one rounding to bf16, one 8-byte store per 4 channels.
-  const int64_t N = args.n;
+  uint8_t* wout = buf(wave / kWavesPerBuf) + (wave % kWavesPerBuf) * kWaveOutBytes;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int ml = wm * WTM + j * 32 + (lane & 31);
-    const int m = m0 + ml;
-    const float sa = epi_sa[ml];
+    const int r = j * 32 + (lane & 31);  // row within the wave tile
+    const float sa = r_sa[j];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nl = wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
-        const float4 sw4 = *reinterpret_cast<const float4*>(epi_sw + nl);
-        const float4 b4 = *reinterpret_cast<const float4*>(epi_b + nl);
+        const int c8 = i * 32 + 8 * q + 4 * (lane >> 5);  // column within the wave tile
+        const float4 sw4 = r_sw[i][q];
+        const float4 b4 = r_b[i][q];
         const v16f& a = acc[i][j];
         const float o0 = __builtin_fmaf(a[4 * q + 0] * sa, sw4.x, b4.x);
         const float o1 = __builtin_fmaf(a[4 * q + 1] * sa, sw4.y, b4.y);
         const float o2 = __builtin_fmaf(a[4 * q + 2] * sa, sw4.z, b4.z);
         const float o3 = __builtin_fmaf(a[4 * q + 3] * sa, sw4.w, b4.w);
-        if (m < args.m && n0 + nl < args.n)
-          *reinterpret_cast<uint2*>(args.out + (int64_t)m * N + n0 + nl) =
-              make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        const int chunk = c8 >> 3, half = (c8 >> 2) & 1;
+        *reinterpret_cast<uint2*>(wout + r * (RC * 16) + ((chunk ^ (r % RC)) << 4) + (half << 3)) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
       }
     }
   }
+  // own region only: LDS executes one wave's accesses in order, no barrier needed
+  const int64_t N = args.n;
+  constexpr int kRowsPerStore = 64 / RC;
+#pragma unroll
+  for (int t = 0; t < WTM / kRowsPerStore; ++t) {
+    const int r = t * kRowsPerStore + lane / RC;
+    const int c = lane % RC;
+    const uint4 v = *reinterpret_cast<const uint4*>(wout + r * (RC * 16) + ((c ^ (r % RC)) << 4));
+    const int m = m0 + wm * WTM + r;
+    const int n = n0 + wn * WTN + c * 8;
+    if (m < args.m && n < args.n) *reinterpret_cast<uint4*>(args.out + (int64_t)m * N + n) = v;
+  }
 }
 
-template <int BM, int BN, int WM, int WN, int S, int GM>
+template <int BM, int BN, int WM, int WN, int S, int BK, int GM>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
   const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_kernel<BM, BN, WM, WN, S, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
-// id, tile_m, tile_n, waves, stages, name
+// id, tile_m, tile_n, waves, stages, name (every stage holds 128 bytes of k)
 const GemmConfig kConfigs[] = {
-    {0, 256, 256, 8, 4, "bm256_bn256_w4x2_s4"},
-    {1, 256, 256, 8, 5, "bm256_bn256_w2x4_s5"},
-    {2, 256, 128, 8, 6, "bm256_bn128_w4x2_s6"},
-    {3, 128, 256, 8, 6, "bm128_bn256_w2x4_s6"},
-    {4, 128, 128, 4, 4, "bm128_bn128_w2x2_s4"},
-    {5, 64, 64, 4, 4, "bm64_bn64_w2x2_s4"},
+    {0, 256, 256, 8, 2, "bm256_bn256_w2x4_s2"},
+    {1, 256, 128, 8, 3, "bm256_bn128_w4x2_s3"},
+    {2, 128, 256, 8, 3, "bm128_bn256_w2x4_s3"},
+    {3, 128, 128, 4, 2, "bm128_bn128_w2x2_s2"},
+    {4, 64, 64, 4, 3, "bm64_bn64_w2x2_s3"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -367,12 +470,11 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
                        hipStream_t stream) {
   GemmArgs a{qa, a_scale, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
   switch (id) {
-    case 0: return launch<256, 256, 4, 2, 4, 4>(a, stream);
-    case 1: return launch<256, 256, 2, 4, 5, 4>(a, stream);
-    case 2: return launch<256, 128, 4, 2, 6, 4>(a, stream);
-    case 3: return launch<128, 256, 2, 4, 6, 4>(a, stream);
-    case 4: return launch<128, 128, 2, 2, 4, 8>(a, stream);
-    case 5: return launch<64, 64, 2, 2, 4, 8>(a, stream);
+    case 0: return launch<256, 256, 2, 4, 2, 128, 4>(a, stream);
+    case 1: return launch<256, 128, 4, 2, 3, 128, 4>(a, stream);
+    case 2: return launch<128, 256, 2, 4, 3, 128, 4>(a, stream);
+    case 3: return launch<128, 128, 2, 2, 2, 128, 8>(a, stream);
+    case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
