@@ -1,0 +1,144 @@
+"""Summaries of rocprofv3 output for the committed performance record.
+
+    python -m fp8_w8a8_quantized_token_amd.profiling stats <kernel_stats.csv> --command "<cmd>" [--out file.md]
+    python -m fp8_w8a8_quantized_token_amd.profiling traffic <fetch counter csv> <write counter csv>
+        --kernel <substring> --command "<cmd>" [--out file.md] [--json file.json]
+
+``stats`` renders rocprofv3's ``--kernel-trace --stats`` table (calls, average and
+min/max duration per kernel). ``traffic`` turns ``--pmc FETCH_SIZE`` and
+``--pmc WRITE_SIZE`` runs into HBM bytes per launch of one kernel, scaled by what
+the same counters read for a plain 1 GiB device copy in the same run (the bench's
+``--copy-calibration`` launches), and records the SHA-256 of the GEMM source the
+counters were taken on so that stale figures are not reported as current.
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCE = os.path.join(PKG_DIR, "csrc", "gemm_fp8.hip")
+CALIBRATION_BYTES = 1 << 30  # the bench's copy calibration moves 1 GiB per launch
+
+
+def _short(name, width=90):
+    name = name.replace("fp8w8a8::(anonymous namespace)::", "")
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def stats_markdown(path, command):
+    rows = list(csv.DictReader(open(path)))
+    out = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+           "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel(path, counter):
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return per
+
+
+def _calibration(per):
+    """KiB reported per 1 GiB device copy (the largest-grid copy launches)."""
+    vals = []
+    for name, v in per.items():
+        if "copyBuffer" in name or "copy" in name.lower():
+            big = [x for g, x in v if x > 100_000]  # > ~100 MiB: the 1 GiB calibration copies
+            vals += big
+    if not vals:
+        raise ValueError("no calibration copy found in the counter run")
+    return statistics.median(vals)
+
+
+def traffic(fetch_csv, write_csv, kernel):
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    cal_fetch = _calibration(fetch)
+    cal_write = _calibration(write)
+    f_vals = [x for name, v in fetch.items() if kernel in name for _, x in v]
+    w_vals = [x for name, v in write.items() if kernel in name for _, x in v]
+    if not f_vals or not w_vals:
+        raise ValueError(f"kernel {kernel!r} not found in the counter runs")
+    fetch_scale = CALIBRATION_BYTES / (cal_fetch * 1024)
+    write_scale = CALIBRATION_BYTES / (cal_write * 1024)
+    fetch_bytes = statistics.median(f_vals) * 1024 * fetch_scale
+    write_bytes = statistics.median(w_vals) * 1024 * write_scale
+    return {
+        "kernel": kernel,
+        "launches": len(f_vals),
+        "fetch_kib_raw_median": statistics.median(f_vals),
+        "write_kib_raw_median": statistics.median(w_vals),
+        "calibration_copy_fetch_kib": cal_fetch,
+        "calibration_copy_write_kib": cal_write,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "fetch_bytes_per_launch": fetch_bytes,
+        "write_bytes_per_launch": write_bytes,
+        "hbm_bytes_per_launch": fetch_bytes + write_bytes,
+        "gemm_source_sha256": hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest(),
+    }
+
+
+def traffic_markdown(t, command, algorithmic=None):
+    out = ["# rocprofv3 HBM traffic (FETCH_SIZE / WRITE_SIZE)", "", f"Command: `{command}`", "",
+           f"Kernel filter: `{t['kernel']}` ({t['launches']} launches, medians)", "",
+           "Scale: the counters' reading for a plain 1 GiB device copy in the same run",
+           f"(FETCH {t['calibration_copy_fetch_kib']:.0f} KiB, WRITE {t['calibration_copy_write_kib']:.0f} KiB per 1 GiB)",
+           f"gives fetch x{t['fetch_scale']:.3f}, write x{t['write_scale']:.3f}.", "",
+           "| quantity | value |", "|---|---|",
+           f"| FETCH_SIZE raw (KiB / launch) | {t['fetch_kib_raw_median']:.0f} |",
+           f"| WRITE_SIZE raw (KiB / launch) | {t['write_kib_raw_median']:.0f} |",
+           f"| fetched bytes / launch (scaled) | {t['fetch_bytes_per_launch'] / 1e6:.2f} MB |",
+           f"| written bytes / launch (scaled) | {t['write_bytes_per_launch'] / 1e6:.2f} MB |",
+           f"| HBM bytes / launch | {t['hbm_bytes_per_launch'] / 1e6:.2f} MB |"]
+    if algorithmic:
+        out.append(f"| algorithmic bytes / launch | {algorithmic / 1e6:.2f} MB |")
+        out.append(f"| traffic / algorithmic | {t['hbm_bytes_per_launch'] / algorithmic:.2f} |")
+    out += ["", f"GEMM source SHA-256 at measurement: `{t['gemm_source_sha256']}`"]
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--command", required=True)
+    a.add_argument("--out")
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--command", required=True)
+    b.add_argument("--algorithmic", type=float)
+    b.add_argument("--out")
+    b.add_argument("--json")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        text = stats_markdown(args.csv, args.command)
+    else:
+        t = traffic(args.fetch_csv, args.write_csv, args.kernel)
+        text = traffic_markdown(t, args.command, args.algorithmic)
+        if args.json:
+            with open(args.json, "w") as f:
+                json.dump(dict(t, command=args.command), f, indent=1)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,113 @@
+"""The oracle's pins catch plausible mistakes: each test plants one mistake in the
+oracle (on the CPU, through monkeypatch) and checks that a pin fails.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.e4m3 as e4m3_mod
+import oracle.linear as linear_mod
+import oracle.quant as quant_mod
+from tests import test_oracle_e4m3 as te
+from tests import test_oracle_linear as tl
+from tests import test_oracle_quant as tq
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_round_half_up_is_caught(monkeypatch):
+    def encode_half_up(values):
+        # the same steps as the oracle's encode with ties rounded away from zero
+        v = np.asarray(values, np.float32).astype(np.float64)
+        neg = np.signbit(v)
+        a = np.minimum(np.abs(v), 448.0)
+        sub = np.floor(a * 512.0 + 0.5)
+        safe = np.where(a >= 2.0 ** -6, a, 1.0)
+        _, e = np.frexp(safe)
+        e = e.astype(np.int64) - 1
+        m = np.floor((safe / np.exp2(e.astype(np.float64)) - 1.0) * 8.0 + 0.5).astype(np.int64)
+        e = np.where(m == 8, e + 1, e)
+        m = np.where(m == 8, 0, m)
+        code = np.where(a < 2.0 ** -6, sub.astype(np.int64), ((e + 7) << 3) | m)
+        return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+    monkeypatch.setattr(e4m3_mod, "encode", encode_half_up)
+    _fails(te.test_encode_matches_brute_force_at_every_boundary)
+
+
+def test_missing_saturation_is_caught(monkeypatch):
+    real = e4m3_mod.encode
+
+    def encode_no_clamp(values):
+        v = np.asarray(values, np.float32)
+        out = real(v)
+        return np.where(np.abs(v) > 448, np.uint8(0x7F) | (out & 0x80), out).astype(np.uint8)
+
+    monkeypatch.setattr(e4m3_mod, "encode", encode_no_clamp)
+    _fails(te.test_saturation_and_ties)
+
+
+def test_lost_sign_of_zero_is_caught(monkeypatch):
+    real = e4m3_mod.encode
+    monkeypatch.setattr(e4m3_mod, "encode", lambda v: np.where(real(v) == 0x80, 0, real(v)).astype(np.uint8))
+    _fails(tq.test_zero_rows_and_signed_zero)
+
+
+def test_int8_denominator_is_caught(monkeypatch):
+    monkeypatch.setattr(quant_mod, "_F448", np.float32(127.0))
+    _fails(tq.test_worked_rows, GOLDEN)
+
+
+def test_multiply_by_reciprocal_is_caught(monkeypatch):
+    # x * (1/s) instead of the correctly rounded x / s differs near rounding boundaries
+    real_encode = e4m3_mod.encode
+
+    def quant_recip(x_f32):
+        x = np.asarray(x_f32, np.float32)
+        s = quant_mod.row_scales(x)
+        q = np.empty(x.shape, np.uint8)
+        nz = s > 0
+        r = (np.float32(1.0) / s[nz]).astype(np.float32)
+        q[nz] = real_encode((x[nz] * r[:, None]).astype(np.float32))
+        q[~nz] = np.signbit(x[~nz]).astype(np.uint8) << 7
+        return q, s
+
+    monkeypatch.setattr(quant_mod, "quant_rows_f32", quant_recip)
+    _fails(tq.test_hard_quotients_match_torch)
+
+
+def test_reversed_k_pairing_is_caught(monkeypatch):
+    # a wrong operand index: activation k paired with weight k' = K - 1 - k
+    def gemm_misindexed(qa, qw):
+        d = e4m3_mod.decode
+        return d(qa)[:, ::-1] @ d(qw).T
+    monkeypatch.setattr(linear_mod, "gemm_exact", gemm_misindexed)
+    _fails(tl.test_linear_matches_python_loops)
+
+
+def test_dropped_bias_is_caught(monkeypatch):
+    real = linear_mod.epilogue
+    monkeypatch.setattr(linear_mod, "epilogue", lambda acc, sa, sw, b=None: real(acc, sa, sw, None))
+    _fails(tl.test_zero_activation_gives_bias)
+
+
+def test_scales_on_swapped_axes_are_caught(monkeypatch):
+    def epilogue_swapped(acc, a_scale, w_scale, bias_bits=None):
+        acc = np.asarray(acc, np.float64)
+        return acc * np.resize(np.asarray(w_scale, np.float64), acc.shape[0])[:, None] * \
+            np.resize(np.asarray(a_scale, np.float64), acc.shape[1])[None, :]
+    monkeypatch.setattr(linear_mod, "epilogue", epilogue_swapped)
+    _fails(tl.test_bias_none_and_scales_broadcast_along_the_right_axes)
+
+
+def test_amax_without_abs_is_caught(monkeypatch):
+    def row_scales_signed(x_f32):
+        x = np.asarray(x_f32, np.float32)
+        return (np.max(x, axis=1).astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    monkeypatch.setattr(quant_mod, "row_scales", row_scales_signed)
+    _fails(tq.test_invariants)

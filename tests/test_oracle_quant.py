@@ -86,6 +86,47 @@ def test_extreme_magnitude_rows_match_torch():
     assert np.array_equal(s, ts) and np.array_equal(q, tq)
 
 
+def hard_quotient_rows(count=200, seed=0):
+    """Rows [amax, x...] whose quotients x / s and x * (1 / s) round to different codes.
+
+    Found with plain numpy arithmetic and torch's float8 cast (no oracle code): these are
+    the elements where a divide-free shortcut would go wrong, so the oracle is held to
+    the correctly rounded quotient exactly where it matters.
+    """
+    pat = np.arange(1 << 16, dtype=np.uint32)
+    x = (pat << 16).view(np.float32)
+    x = x[np.isfinite(x)]
+
+    def enc(v):
+        return torch.from_numpy(np.clip(v, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy()
+
+    rows = []
+    rng = np.random.default_rng(seed)
+    for a_bits in rng.integers(0x3000, 0x5000, count):
+        amax = np.float32((np.uint32(a_bits) << 16).view(np.float32))
+        xs = x[np.abs(x) <= amax]
+        s = np.float32(amax / np.float32(448))
+        r = np.float32(np.float32(1) / s)
+        d = np.flatnonzero(enc((xs / s).astype(np.float32)) != enc((xs * r).astype(np.float32)))
+        if len(d):
+            row = np.zeros(8, np.float32)
+            row[0] = amax
+            picks = xs[d[:7]]
+            row[1:1 + len(picks)] = picks
+            rows.append(row)
+    return np.stack(rows)
+
+
+def test_hard_quotients_match_torch():
+    rows = hard_quotient_rows()
+    assert len(rows) >= 10
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    q, s = quant.quant_rows(bf16_bits(x))
+    tq, ts = _torch_quant(x)
+    assert np.array_equal(s, ts) and np.array_equal(q, tq)
+
+
 def test_invariants():
     case = make_case(96, 16, 1024, seed=9, kind="outlier")
     bits = bf16_bits(case.a)
