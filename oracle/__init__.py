@@ -16,12 +16,14 @@ Modules
   e4m3    decode / round-to-nearest-even saturating encode of OCP e4m3fn codes
   quant   per-row (per-token, per-channel) amax -> scale -> code quantisation
   linear  exact float64 FP8 product and the scale/bias epilogue
+  act     GELU / SiLU rounded exactly to bf16 (the producer upstream of the FFN-down
+          linear), then the per-token quantiser: the fused producer's result
 
 Every function here is pinned by tests under ``tests/`` against facts fixed
 outside this package (the format definition, torch's CPU float8 cast, brute
 force, closed forms and invariants); nothing here is "parity unpinned".
 """
 
-from . import e4m3, quant, linear  # noqa: F401
+from . import e4m3, quant, linear, act  # noqa: F401
 
-__all__ = ["e4m3", "quant", "linear"]
+__all__ = ["e4m3", "quant", "linear", "act"]

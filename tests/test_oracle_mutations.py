@@ -2,12 +2,15 @@
 oracle (on the CPU, through monkeypatch) and checks that a pin fails.
 """
 
+import mpmath
 import numpy as np
 import pytest
 
+import oracle.act as act_mod
 import oracle.e4m3 as e4m3_mod
 import oracle.linear as linear_mod
 import oracle.quant as quant_mod
+from tests import test_oracle_act as ta
 from tests import test_oracle_e4m3 as te
 from tests import test_oracle_linear as tl
 from tests import test_oracle_quant as tq
@@ -111,3 +114,78 @@ def test_amax_without_abs_is_caught(monkeypatch):
         return (np.max(x, axis=1).astype(np.float32) / np.float32(448.0)).astype(np.float32)
     monkeypatch.setattr(quant_mod, "row_scales", row_scales_signed)
     _fails(tq.test_invariants)
+
+
+# --- activation producers (oracle.act): mistakes planted in the exact evaluation
+
+
+def _act_sample():
+    rng = np.random.default_rng(11)
+    pats = act_mod._finite_patterns()
+    return np.sort(rng.choice(pats, 1500, replace=False)).astype(np.uint16)
+
+
+def _act_planted(monkeypatch, kind, wrong):
+    real = act_mod._act_mp
+    monkeypatch.setattr(act_mod, "_act_mp", lambda x, k: wrong(x) if k == kind else real(x, k))
+    pats = _act_sample()
+    return pats, act_mod.act_bits_exact(pats, kind)
+
+
+def test_gelu_erf_wrong_sign_is_caught(monkeypatch):
+    pats, vals = _act_planted(monkeypatch, "gelu_erf", lambda x: x * mpmath.erfc(x / mpmath.sqrt(2)) / 2)
+    _fails(ta.check_against_float64, "gelu_erf", pats, vals)
+
+
+def test_gelu_tanh_wrong_constant_is_caught(monkeypatch):
+    def wrong(x):
+        u = mpmath.sqrt(2 / mpmath.pi) * (x + mpmath.mpf("0.0447") * x ** 3)
+        return x / (1 + mpmath.exp(-2 * u))
+    pats, vals = _act_planted(monkeypatch, "gelu_tanh", wrong)
+    _fails(ta.check_against_float64, "gelu_tanh", pats, vals)
+
+
+def test_silu_wrong_exponent_sign_is_caught(monkeypatch):
+    pats, vals = _act_planted(monkeypatch, "silu", lambda x: x / (1 + mpmath.exp(x)))
+    _fails(ta.check_against_float64, "silu", pats, vals)
+
+
+def test_float64_evaluation_is_caught(monkeypatch):
+    # evaluating in float64 instead of exactly loses the x^2 term that decides the ties
+    def f64(x):
+        v = float(x)
+        return mpmath.mpf(0.5 * v * float(mpmath.erfc(-v / 2 ** 0.5)))
+    pats, vals = _act_planted(monkeypatch, "gelu_erf", f64)
+    pats = np.concatenate([pats, np.arange(1, 256, dtype=np.uint16)])  # the tiny inputs
+    vals = act_mod.act_bits_exact(pats, "gelu_erf")
+    _fails(ta.check_ties, "gelu_erf", pats, vals)
+
+
+def test_bf16_ties_away_from_zero_are_caught(monkeypatch):
+    real_floor = mpmath.floor
+
+    def round_away(y):
+        y = mpmath.mpf(y)
+        if y == 0:
+            return np.uint16(0)
+        neg = y < 0
+        a = -y if neg else y
+        _, e = mpmath.frexp(a)
+        qe = max(int(e) - 8, -133)
+        f = real_floor(mpmath.ldexp(a, -qe) + mpmath.mpf(0.5))
+        val = float(mpmath.ldexp(f, qe))
+        bits = np.array([val], np.float32).view(np.uint32)[0] >> np.uint32(16)
+        return np.uint16(bits | (0x8000 if neg else 0))
+    monkeypatch.setattr(act_mod, "round_bf16", round_away)
+    _fails(ta.test_round_bf16_matches_torch_on_float32_values)
+
+
+def test_bf16_without_subnormals_is_caught(monkeypatch):
+    real = act_mod.round_bf16
+
+    def flush(y):
+        if isinstance(y, float) and 0 < abs(y) < 2.0 ** -126:
+            return np.uint16(0x8000 if y < 0 else 0)
+        return real(y)
+    monkeypatch.setattr(act_mod, "round_bf16", flush)
+    _fails(ta.test_round_bf16_matches_torch_on_float32_values)
