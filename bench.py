@@ -16,6 +16,12 @@ with events only at the two ends of the region. `roofline` is the GEMM kernel (t
 dominant launch): a second region of K steps records HIP events on the launch
 stream around every launch, giving each kernel's average launch duration.
 `cpu_baseline` times the CPU oracle (numpy, float64) on the same workload.
+
+`producer` (outside the step) times the activation producer that feeds the
+FFN-down linear: GELU (tanh form) of the FFN-up output followed by per-token
+e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
+output, then the plain quantiser), at the FFN-down input [4096, 8192] and at the
+DiT-block size [32760, 8192].
 """
 
 import argparse
@@ -58,6 +64,57 @@ def traffic_from_profile():
         return float(t["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
+
+
+def producer_bench(torch, fp8, lib, dev, stream, steps):
+    """Fused GELU -> per-token FP8 producer against the unfused pair, HBM-resident inputs."""
+    from fp8_w8a8_quantized_token_amd import _lib
+    from workloads.synth import activation
+    table = fp8.act_table("gelu_tanh", dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def call(st, name):
+        if st:
+            raise _lib.Fp8W8A8Error(st, name)
+
+    out = {"activation": "gelu_tanh", "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s", "shapes": []}
+    for rows, cols, nsets in ((4096, 8192, 8), (32760, 8192, 2)):
+        xs = [activation(0, 3, 40 + i, rows, cols, "normal").to(dev) for i in range(nsets)]
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        sc = torch.empty((rows,), dtype=torch.float32, device=dev)
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+
+        def fused(i):
+            call(lib.fp8_act_quant_rows(p(xs[i % nsets]), rows, cols, p(table), p(q), p(sc), sptr),
+                 "fp8_act_quant_rows")
+
+        def unfused(i):
+            call(lib.fp8_act_rows(p(xs[i % nsets]), rows, cols, p(table), p(y), sptr), "fp8_act_rows")
+            call(lib.fp8_quant_rows(p(y), rows, cols, p(q), p(sc), sptr), "fp8_quant_rows")
+
+        res = {}
+        for name, fn in (("fused", fused), ("unfused", unfused)):
+            for i in range(5):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / steps
+        algo = quant_bytes(rows, cols)
+        gbps = algo / (res["fused"] * 1e-6) / 1e9
+        out["shapes"].append({
+            "rows": rows, "cols": cols, "fused_us": round(res["fused"], 2), "unfused_us": round(res["unfused"], 2),
+            "speedup": round(res["unfused"] / res["fused"], 3), "algorithmic_bytes_per_launch": algo,
+            "achieved": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+        })
+        del xs, q, sc, y
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(budget_s=20.0):
@@ -107,6 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run 3 plain 1 GiB device-to-device copies (a known-size kernel "
                          "for scaling HBM counter readings)")
@@ -237,6 +295,10 @@ def main():
         },
         "gemm_median_us": round(gemm_ms[len(gemm_ms) // 2] * 1e3, 3),
     }
+    if not args.no_producer:
+        del sets
+        torch.cuda.empty_cache()
+        result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if args.copy_calibration:
         src = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -10,7 +10,11 @@ from ._lib import Fp8W8A8Error, LIB_PATH, lib  # noqa: F401
 from .ops import (  # noqa: F401
     A_BF16,
     A_E4M3,
+    ACTIVATIONS,
     Fp8Linear,
+    act_quant_rows,
+    act_rows,
+    act_table,
     gemm_config_count,
     gemm_run_config,
     linear,
@@ -21,6 +25,10 @@ from .ops import (  # noqa: F401
 __all__ = [
     "Fp8Linear",
     "Fp8W8A8Error",
+    "ACTIVATIONS",
+    "act_table",
+    "act_rows",
+    "act_quant_rows",
     "linear",
     "quant_rows",
     "quant_weights_per_channel",

@@ -22,6 +22,11 @@ ERR_HIP = -6
 A_BF16 = 0
 A_E4M3 = 1
 
+ACT_GELU_ERF = 1
+ACT_GELU_TANH = 2
+ACT_SILU = 3
+ACT_TABLE_BYTES = 131072
+
 MAX_ROWS = 1 << 24
 MAX_DIM = 1 << 20
 
@@ -33,6 +38,9 @@ SIGNATURES = {
     "fp8w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8_quant_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_quant_weights_per_channel": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "fp8_act_table_build": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p]),
+    "fp8_act_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "fp8_act_quant_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "fp8_linear_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.POINTER(_c_p)]),
     "fp8_linear_workspace_bytes": (ctypes.c_size_t, [_c_p, _c_i64]),
     "fp8_linear_run": (ctypes.c_int, [_c_p, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),

@@ -56,10 +56,14 @@ int query_device(int device, int* cus) {
   return st == 1 ? FP8W8A8_OK : FP8W8A8_ERR_BAD_DEVICE;
 }
 
-int current_device_ok() {
+int current_device_ok(int* cus = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP8W8A8_ERR_HIP;
-  return query_device(dev, nullptr);
+  return query_device(dev, cus);
+}
+
+bool valid_act(int act) {
+  return act == FP8W8A8_ACT_GELU_ERF || act == FP8W8A8_ACT_GELU_TANH || act == FP8W8A8_ACT_SILU;
 }
 
 int check_quant_args(const void* x, int64_t rows, int64_t cols, const void* q, const float* scale) {
@@ -153,6 +157,45 @@ int fp8_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, void* q_out, 
   if (st != FP8W8A8_OK) return st;
   hipError_t e = launch_quant_rows(static_cast<const uint16_t*>(x_bf16), rows, cols,
                                    static_cast<uint8_t*>(q_out), scale_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_act_table_build(int act, void* table, void* stream) {
+  if (!table || !valid_act(act)) return FP8W8A8_ERR_INVALID_ARG;
+  if (!aligned(table, 16)) return FP8W8A8_ERR_MISALIGNED;
+  int st = current_device_ok();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_act_table(act, static_cast<uint16_t*>(table), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_act_rows(const void* x_bf16, int64_t rows, int64_t cols, const void* table, void* y_bf16, void* stream) {
+  if (!x_bf16 || !table || !y_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  if (rows < 0 || rows >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (cols < 16 || cols > FP8W8A8_MAX_DIM || cols % 16 != 0) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(table, 16) || !aligned(y_bf16, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (rows == 0) return FP8W8A8_OK;
+  int cus = 0;
+  int st = current_device_ok(&cus);
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_act_rows(static_cast<const uint16_t*>(x_bf16), rows * cols, static_cast<const uint16_t*>(table),
+                                 static_cast<uint16_t*>(y_bf16), cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_act_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, const void* table, void* q_out,
+                       float* scale_out, void* stream) {
+  if (!table) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_quant_args(x_bf16, rows, cols, q_out, scale_out);
+  if (st != FP8W8A8_OK) return st;
+  if (!aligned(table, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (rows == 0) return FP8W8A8_OK;
+  int cus = 0;
+  st = current_device_ok(&cus);
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_act_quant_rows(static_cast<const uint16_t*>(x_bf16), rows, cols,
+                                       static_cast<const uint16_t*>(table), static_cast<uint8_t*>(q_out), scale_out,
+                                       cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 

@@ -13,6 +13,17 @@ namespace fp8w8a8 {
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                              hipStream_t stream);
 
+// Build the 65536-entry bf16 -> bf16 table of activation `act` (FP8W8A8_ACT_*).
+hipError_t launch_act_table(int act, uint16_t* table, hipStream_t stream);
+
+// y = table[x] elementwise over `elems` bf16 values (elems % 16 == 0, 16-byte aligned).
+hipError_t launch_act_rows(const uint16_t* x, int64_t elems, const uint16_t* table, uint16_t* y, int cus,
+                           hipStream_t stream);
+
+// The fused producer: per-token quantisation of table[x] (same arguments as launch_quant_rows).
+hipError_t launch_act_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* table, uint8_t* q,
+                                 float* scale, int cus, hipStream_t stream);
+
 // One compiled GEMM kernel configuration.
 struct GemmConfig {
   int id;

@@ -12,7 +12,9 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import A_BF16, A_E4M3, check, lib
+from ._lib import A_BF16, A_E4M3, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU, ACT_TABLE_BYTES, check, lib
+
+ACTIVATIONS = {"gelu_erf": ACT_GELU_ERF, "gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
 
 
 def _stream(t):
@@ -62,6 +64,58 @@ def quant_weights_per_channel(w):
     s = torch.empty((n,), dtype=torch.float32, device=w.device)
     check(lib().fp8_quant_weights_per_channel(_ptr(w), n, k, _ptr(q), _ptr(s), _stream(w)),
           "fp8_quant_weights_per_channel")
+    return q, s
+
+
+def act_table(kind, device=None):
+    """Build the bf16 -> bf16 table of activation `kind` ("gelu_erf", "gelu_tanh", "silu") on a GPU.
+
+    Returns an int16 tensor [65536] indexed by the input's bit pattern; pass it to
+    act_rows / act_quant_rows on the same device and keep it alive while they run.
+    """
+    if kind not in ACTIVATIONS:
+        raise ValueError(f"unknown activation {kind!r}; expected one of {sorted(ACTIVATIONS)}")
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    t = torch.empty(ACT_TABLE_BYTES // 2, dtype=torch.int16, device=device)
+    with torch.cuda.device(t.device):
+        check(lib().fp8_act_table_build(ACTIVATIONS[kind], _ptr(t), _stream(t)), "fp8_act_table_build")
+    return t
+
+
+def _check_table(table, x):
+    _require(table, (torch.int16,), "table", 1)
+    if table.numel() != ACT_TABLE_BYTES // 2 or table.device != x.device:
+        raise ValueError("table must be the int16 [65536] tensor act_table built on x's device")
+
+
+def act_rows(x, table, out=None):
+    """The unfused producer: bf16 act(x) rounded to bf16, same shape as x."""
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    _require(x2, (torch.bfloat16,), "x", 2)
+    _check_table(table, x2)
+    m, k = x2.shape
+    y = torch.empty((m, k), dtype=torch.bfloat16, device=x2.device) if out is None else out
+    _require(y, (torch.bfloat16,), "out")
+    if y.numel() != m * k:
+        raise ValueError("out must hold as many elements as x")
+    check(lib().fp8_act_rows(_ptr(x2), m, k, _ptr(table), _ptr(y), _stream(x2)), "fp8_act_rows")
+    return y.view(x.shape)
+
+
+def act_quant_rows(x, table, q=None, scale=None):
+    """The fused producer: per-token FP8 (codes uint8 [m, k], scales fp32 [m]) of act(x) rounded to bf16."""
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    _require(x2, (torch.bfloat16,), "x", 2)
+    _check_table(table, x2)
+    m, k = x2.shape
+    q = torch.empty((m, k), dtype=torch.uint8, device=x2.device) if q is None else _codes(q)
+    s = torch.empty((m,), dtype=torch.float32, device=x2.device) if scale is None else scale
+    _require(q, (torch.uint8,), "q")
+    _require(s, (torch.float32,), "scale")
+    if q.numel() != m * k or s.numel() != m:
+        raise ValueError("q must hold m * k codes and scale m values")
+    check(lib().fp8_act_quant_rows(_ptr(x2), m, k, _ptr(table), _ptr(q), _ptr(s), _stream(x2)),
+          "fp8_act_quant_rows")
     return q, s
 
 

@@ -98,6 +98,63 @@ int fp8_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, void* q_out, 
 int fp8_quant_weights_per_channel(const void* w_bf16, int64_t n, int64_t k, void* w_fp8_out,
                                   float* w_scale_out, void* stream);
 
+/* ---- activation producers that emit FP8 ----------------------------------------
+ *
+ * HunyuanVideo1.5 retrospective, section 3, item 5 (producer fusion): the GELU or
+ * SiLU in front of the FFN-down linear can hand the FP8 linear its (e4m3fn codes,
+ * per-token scale) pair directly, instead of writing bf16 that a separate pass
+ * quantises. The result is defined as the unfused path's:
+ *
+ *   y[r,c]          = bf16_rne(act(x[r,c]))   (the exact function value, rounded once)
+ *   (q_out, scale)  = fp8_quant_rows(y)        (bit for bit)
+ *
+ * The page names "GELU/SiLU" and no formula; three textbook functions are offered:
+ *   FP8W8A8_ACT_GELU_ERF   x * Phi(x) = x/2 * erfc(-x / sqrt 2)
+ *   FP8W8A8_ACT_GELU_TANH  x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ *   FP8W8A8_ACT_SILU       x / (1 + exp(-x))
+ * A bf16 -> bf16 function is a 65536-entry table: the caller allocates it
+ * (FP8W8A8_ACT_TABLE_BYTES, device memory, 16-byte aligned), builds it once per
+ * device with fp8_act_table_build, keeps it alive while producers use it, and
+ * passes it to every producer call. Entries for finite inputs are the correctly
+ * rounded bf16 of the function; non-finite inputs are outside the contract (the
+ * table maps NaN to NaN, +inf to +inf and -inf to -0, and the quantiser's codes
+ * for them are unspecified).
+ */
+#define FP8W8A8_ACT_GELU_ERF 1
+#define FP8W8A8_ACT_GELU_TANH 2
+#define FP8W8A8_ACT_SILU 3
+#define FP8W8A8_ACT_TABLE_BYTES 131072 /* 65536 bf16 entries, indexed by the input's bit pattern */
+
+/*
+ * fp8_act_table_build - fill `table` (device, FP8W8A8_ACT_TABLE_BYTES, 16-byte
+ * aligned, written) with bf16_rne(act(x)) for every bf16 bit pattern x, on the
+ * current device, asynchronously on `stream`. An unknown act is
+ * FP8W8A8_ERR_INVALID_ARG.
+ */
+int fp8_act_table_build(int act, void* table, void* stream);
+
+/*
+ * fp8_act_rows - the unfused producer: y_bf16[r, c] = table[x_bf16[r, c]].
+ *
+ *   x_bf16   device, bf16 [rows, cols], 16-byte aligned
+ *   rows     0 <= rows < FP8W8A8_MAX_ROWS (0 is a no-op)
+ *   cols     16 <= cols <= FP8W8A8_MAX_DIM, cols % 16 == 0
+ *   table    device, built by fp8_act_table_build, 16-byte aligned (read)
+ *   y_bf16   device, bf16 [rows, cols], 16-byte aligned, written (must not overlap x)
+ */
+int fp8_act_rows(const void* x_bf16, int64_t rows, int64_t cols, const void* table, void* y_bf16,
+                 void* stream);
+
+/*
+ * fp8_act_quant_rows - the fused producer: the codes and scales fp8_quant_rows
+ * would give for fp8_act_rows' output, from one read of x and no bf16 output.
+ * Arguments as fp8_quant_rows, plus `table` (device, built by
+ * fp8_act_table_build, 16-byte aligned, read). Feed q_out / scale_out to
+ * fp8_linear_run with FP8W8A8_A_E4M3.
+ */
+int fp8_act_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, const void* table, void* q_out,
+                       float* scale_out, void* stream);
+
 /*
  * A constructed linear: validated shapes, borrowed weight pointers and the GEMM
  * kernel configuration chosen for each activation-row bucket. The choice is made

@@ -128,3 +128,39 @@ def test_binding_refuses_cpu_tensors():
     from fp8_w8a8_quantized_token_amd import quant_rows
     with pytest.raises(ValueError, match="GPU tensor"):
         quant_rows(torch.zeros((4, 16), dtype=torch.bfloat16))
+
+
+def test_act_producers_validation(lib):
+    A = ALIGNED
+    tb = lib.fp8_act_table_build
+    for bad in (0, 4, -1):
+        assert tb(bad, A, None) == _lib.ERR_INVALID_ARG, bad
+    assert tb(_lib.ACT_SILU, None, None) == _lib.ERR_INVALID_ARG
+    assert tb(_lib.ACT_GELU_ERF, MIS16, None) == _lib.ERR_MISALIGNED
+
+    ar = lib.fp8_act_rows
+    assert ar(None, 4, 16, A, A, None) == _lib.ERR_INVALID_ARG
+    assert ar(A, 4, 16, None, A, None) == _lib.ERR_INVALID_ARG
+    assert ar(A, 4, 16, A, None, None) == _lib.ERR_INVALID_ARG
+    for cols in (0, 8, 24, _lib.MAX_DIM + 16):
+        assert ar(A, 4, cols, A, A, None) == _lib.ERR_BAD_SHAPE, cols
+    assert ar(A, -1, 16, A, A, None) == _lib.ERR_BAD_SHAPE
+    assert ar(MIS16, 4, 16, A, A, None) == _lib.ERR_MISALIGNED
+    assert ar(A, 4, 16, MIS16, A, None) == _lib.ERR_MISALIGNED
+    assert ar(A, 4, 16, A, MIS16, None) == _lib.ERR_MISALIGNED
+    assert ar(A, 0, 16, A, A, None) == _lib.OK
+
+    aq = lib.fp8_act_quant_rows
+    assert aq(A, 4, 16, None, A, A, None) == _lib.ERR_INVALID_ARG
+    assert aq(None, 4, 16, A, A, A, None) == _lib.ERR_INVALID_ARG
+    assert aq(A, 4, 16, A, A, None, None) == _lib.ERR_INVALID_ARG
+    assert aq(A, 4, 24, A, A, A, None) == _lib.ERR_BAD_SHAPE
+    assert aq(A, 4, 16, MIS16, A, A, None) == _lib.ERR_MISALIGNED
+    assert aq(A, 4, 16, A, A, MIS4, None) == _lib.ERR_MISALIGNED
+    assert aq(A, 0, 16, A, A, A, None) == _lib.OK
+
+
+def test_act_binding_rejects_unknown_kind():
+    from fp8_w8a8_quantized_token_amd import act_table
+    with pytest.raises(ValueError, match="unknown activation"):
+        act_table("relu", device="cpu")
