@@ -66,7 +66,10 @@ def traffic_from_profile():
         return None
 
 
-def producer_bench(torch, fp8, lib, dev, stream, steps):
+PRODUCER_SHAPES = ((4096, 8192, 8), (32760, 8192, 2))  # rows, cols, rotating input sets
+
+
+def producer_bench(torch, fp8, lib, dev, stream, steps, only_rows=None):
     """Fused GELU -> per-token FP8 producer against the unfused pair, HBM-resident inputs."""
     from fp8_w8a8_quantized_token_amd import _lib
     from workloads.synth import activation
@@ -79,7 +82,9 @@ def producer_bench(torch, fp8, lib, dev, stream, steps):
             raise _lib.Fp8W8A8Error(st, name)
 
     out = {"activation": "gelu_tanh", "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s", "shapes": []}
-    for rows, cols, nsets in ((4096, 8192, 8), (32760, 8192, 2)):
+    for rows, cols, nsets in PRODUCER_SHAPES:
+        if only_rows is not None and rows != only_rows:
+            continue
         xs = [activation(0, 3, 40 + i, rows, cols, "normal").to(dev) for i in range(nsets)]
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         sc = torch.empty((rows,), dtype=torch.float32, device=dev)
@@ -115,6 +120,16 @@ def producer_bench(torch, fp8, lib, dev, stream, steps):
         del xs, q, sc, y
         torch.cuda.empty_cache()
     return out
+
+
+def copy_calibration(torch, dev):
+    """Three plain 1 GiB device-to-device copies: a kernel of known traffic for scaling counters."""
+    src = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(budget_s=20.0):
@@ -165,6 +180,8 @@ def main():
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
+    ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
+                    help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run 3 plain 1 GiB device-to-device copies (a known-size kernel "
                          "for scaling HBM counter readings)")
@@ -185,6 +202,14 @@ def main():
     lib = _lib.lib()
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    if args.producer_only:
+        res = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)), args.producer_only)
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+            res["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}
+        print(json.dumps({"producer": res}), flush=True)
+        return
 
     # rotating sets: activation bf16, codes + scales, weight plan, output
     sets = []
@@ -300,11 +325,7 @@ def main():
         torch.cuda.empty_cache()
         result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if args.copy_calibration:
-        src = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
