@@ -18,12 +18,14 @@ Modules
   linear  exact float64 FP8 product and the scale/bias epilogue
   act     GELU / SiLU rounded exactly to bf16 (the producer upstream of the FFN-down
           linear), then the per-token quantiser: the fused producer's result
+  w8a16   the FP8 weight-only linear: bf16 activation times the per-channel e4m3fn
+          weight, in float64
 
 Every function here is pinned by tests under ``tests/`` against facts fixed
 outside this package (the format definition, torch's CPU float8 cast, brute
 force, closed forms and invariants); nothing here is "parity unpinned".
 """
 
-from . import e4m3, quant, linear, act  # noqa: F401
+from . import e4m3, quant, linear, act, w8a16  # noqa: F401
 
-__all__ = ["e4m3", "quant", "linear", "act"]
+__all__ = ["e4m3", "quant", "linear", "act", "w8a16"]

@@ -10,10 +10,12 @@ import oracle.act as act_mod
 import oracle.e4m3 as e4m3_mod
 import oracle.linear as linear_mod
 import oracle.quant as quant_mod
+import oracle.w8a16 as w8a16_mod
 from tests import test_oracle_act as ta
 from tests import test_oracle_e4m3 as te
 from tests import test_oracle_linear as tl
 from tests import test_oracle_quant as tq
+from tests import test_oracle_w8a16 as tw
 
 GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
 
@@ -189,3 +191,34 @@ def test_bf16_without_subnormals_is_caught(monkeypatch):
         return real(y)
     monkeypatch.setattr(act_mod, "round_bf16", flush)
     _fails(ta.test_round_bf16_matches_torch_on_float32_values)
+
+
+# --- the FP8 weight-only linear (oracle.w8a16)
+
+
+def test_w8a16_reversed_k_is_caught(monkeypatch):
+    def wrong(a_bits, qw, w_scale, bias_bits=None):
+        a = quant_mod.bf16_bits_to_f32(np.asarray(a_bits, np.uint16)).astype(np.float64)
+        out = (a[:, ::-1] @ e4m3_mod.decode(np.asarray(qw, np.uint8)).T) * np.asarray(w_scale, np.float64)[None, :]
+        if bias_bits is not None:
+            out = out + quant_mod.bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+        return out
+    monkeypatch.setattr(w8a16_mod, "w8a16_ref", wrong)
+    _fails(tw.test_matches_exact_rational_brute_force)
+
+
+def test_w8a16_scale_on_the_token_axis_is_caught(monkeypatch):
+    real = w8a16_mod.w8a16_ref
+
+    def wrong(a_bits, qw, w_scale, bias_bits=None):
+        base = real(a_bits, qw, np.ones_like(np.asarray(w_scale, np.float32)), bias_bits)
+        return base * np.resize(np.asarray(w_scale, np.float64), base.shape[0])[:, None]
+    monkeypatch.setattr(w8a16_mod, "w8a16_ref", wrong)
+    _fails(tw.test_scales_act_per_output_channel)
+
+
+def test_w8a16_dropped_scale_is_caught(monkeypatch):
+    real = w8a16_mod.w8a16_ref
+    monkeypatch.setattr(w8a16_mod, "w8a16_ref",
+                        lambda a, qw, sw, b=None: real(a, qw, np.ones_like(np.asarray(sw, np.float32)), b))
+    _fails(tw.test_equals_w8a8_where_the_activation_quant_is_the_identity)
