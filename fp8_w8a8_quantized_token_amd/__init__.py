@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     A_E4M3,
     ACTIVATIONS,
     Fp8Linear,
+    Fp8WeightOnlyLinear,
     act_quant_rows,
     act_rows,
     act_table,
@@ -20,11 +21,16 @@ from .ops import (  # noqa: F401
     linear,
     quant_rows,
     quant_weights_per_channel,
+    w8a16_config_count,
+    w8a16_run_config,
 )
 
 __all__ = [
     "Fp8Linear",
     "Fp8W8A8Error",
+    "Fp8WeightOnlyLinear",
+    "w8a16_config_count",
+    "w8a16_run_config",
     "ACTIVATIONS",
     "act_table",
     "act_rows",

@@ -26,9 +26,19 @@ struct fp8_linear_plan {
   const uint16_t* bias;
   int cu_count;
   // m buckets: rows <= max_m[b] use config[b]; the last bucket is unbounded
-  static constexpr int kBuckets = 6;
-  int64_t max_m[kBuckets];
-  int config[kBuckets];
+  int64_t max_m[6];
+  int config[6];
+};
+
+struct fp8_w8a16_plan {
+  int device;
+  int64_t n, k;
+  const uint8_t* w;
+  const float* w_scale;
+  const uint16_t* bias;
+  int cu_count;
+  int64_t max_m[6];
+  int config[6];
 };
 
 namespace {
@@ -82,14 +92,27 @@ int check_weight_args(int64_t n, int64_t k, const void* w, const float* w_scale,
   return FP8W8A8_OK;
 }
 
-bool grid_fits(int config, int64_t m, int64_t n) {
-  return gemm_workgroups(config, m, n) * gemm_threads(config) < kMaxGridThreads;
+// A family of compiled GEMM configurations (the W8A8 GEMM, the W8A16 GEMM) as the
+// selector sees it.
+struct Family {
+  int (*count)();
+  const GemmConfig* (*config)(int);
+  int64_t (*workgroups)(int, int64_t, int64_t);
+  int (*threads)(int);
+};
+const Family kW8A8{gemm_config_count, gemm_config, gemm_workgroups, gemm_threads};
+const Family kW8A16{w8a16_config_count, w8a16_config, w8a16_workgroups, w8a16_threads};
+
+bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
+  return f.workgroups(config, m, n) * f.threads(config) < kMaxGridThreads;
 }
+bool grid_fits(int config, int64_t m, int64_t n) { return grid_fits(kW8A8, config, m, n); }
 
 // Relative throughput of one workgroup of each configuration when it has a CU to
 // itself, and how many of its workgroups share a CU (LDS / register bound). Measured
 // on MI355X: the 256 x 256 tiles run at the highest per-CU rate, 256 x 128 and
-// 128 x 256 close to it, the 4-wave 128 x 128 and 64 x 64 tiles well below.
+// 128 x 256 close to it, the 4-wave 128 x 128 and 64 x 64 tiles well below. Both
+// families order their configurations the same way.
 struct TileModel {
   double eff;
   int per_cu;
@@ -106,27 +129,48 @@ TileModel tile_model(int config) {
 
 // Estimated time (arbitrary units) of configuration c on an m x n output: rounds of
 // co-resident tiles times the work of one round.
-double model_time(int c, int64_t m, int64_t n, int cus) {
-  const GemmConfig* g = gemm_config(c);
+double model_time(const Family& f, int c, int64_t m, int64_t n, int cus) {
+  const GemmConfig* g = f.config(c);
   const TileModel t = tile_model(c);
-  const int64_t tiles = gemm_workgroups(c, m, n);
+  const int64_t tiles = f.workgroups(c, m, n);
   const int64_t conc = std::min<int64_t>(t.per_cu, (tiles + cus - 1) / cus);
   const int64_t rounds = (tiles + cus * conc - 1) / (cus * conc);
   return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n / t.eff;
 }
 
-int choose_config(int64_t m, int64_t n, int cus) {
+int choose_config(const Family& f, int64_t m, int64_t n, int cus) {
   int best = -1;
   double best_t = 0;
-  for (int c = 0; c < gemm_config_count(); ++c) {
-    if (!grid_fits(c, m, n)) continue;
-    const double t = model_time(c, m, n, cus);
+  for (int c = 0; c < f.count(); ++c) {
+    if (!grid_fits(f, c, m, n)) continue;
+    const double t = model_time(f, c, m, n, cus);
     if (best < 0 || t < best_t) {
       best = c;
       best_t = t;
     }
   }
   return best < 0 ? 0 : best;
+}
+
+// m buckets: rows <= bound[b] use the configuration chosen at that bound; the last
+// bucket is unbounded and chosen at 32768 rows.
+constexpr int kBuckets = 6;
+constexpr int64_t kBucketBounds[kBuckets] = {64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
+
+void fill_buckets(const Family& f, int64_t n, int cus, int64_t* max_m, int* config) {
+  for (int b = 0; b < kBuckets; ++b) {
+    max_m[b] = kBucketBounds[b];
+    const int64_t rep = b + 1 < kBuckets ? kBucketBounds[b] : 32768;
+    config[b] = choose_config(f, rep, n, cus);
+  }
+}
+
+int bucket_config(const Family& f, const int64_t* max_m, const int* config, int64_t n, int64_t m) {
+  int b = 0;
+  while (b + 1 < kBuckets && m > max_m[b]) ++b;
+  int c = config[b];
+  if (!grid_fits(f, c, m, n)) c = 0;  // the largest tile launches the fewest workgroups
+  return c;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -222,23 +266,13 @@ int fp8_linear_create(int device, int64_t n, int64_t k, const void* w_fp8, const
   p->w_scale = w_scale;
   p->bias = static_cast<const uint16_t*>(bias_bf16);
   p->cu_count = cus > 0 ? cus : 256;
-  // bucket upper bounds; each bucket's choice is made at its upper bound
-  static const int64_t bounds[fp8_linear_plan::kBuckets] = {64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
-  for (int b = 0; b < fp8_linear_plan::kBuckets; ++b) {
-    p->max_m[b] = bounds[b];
-    const int64_t rep = b + 1 < fp8_linear_plan::kBuckets ? bounds[b] : 32768;
-    p->config[b] = choose_config(rep, n, p->cu_count);
-  }
+  fill_buckets(kW8A8, n, p->cu_count, p->max_m, p->config);
   *out = p;
   return FP8W8A8_OK;
 }
 
 static int plan_bucket_config(const fp8_linear_plan* p, int64_t m) {
-  int b = 0;
-  while (b + 1 < fp8_linear_plan::kBuckets && m > p->max_m[b]) ++b;
-  int c = p->config[b];
-  if (!grid_fits(c, m, p->n)) c = 0;  // the largest tile launches the fewest workgroups
-  return c;
+  return bucket_config(kW8A8, p->max_m, p->config, p->n, m);
 }
 
 size_t fp8_linear_workspace_bytes(const fp8_linear_plan* plan, int64_t m) {
@@ -327,6 +361,75 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
   hipError_t e = launch_gemm(config_id, m, n, k, static_cast<const uint8_t*>(qa), a_scale,
                              static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
                              static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_w8a16_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+                     const void* bias_bf16, fp8_w8a16_plan** out) {
+  if (!out) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  int cus = 0;
+  st = query_device(device, &cus);
+  if (st != FP8W8A8_OK) return st;
+  fp8_w8a16_plan* p = static_cast<fp8_w8a16_plan*>(calloc(1, sizeof(fp8_w8a16_plan)));
+  if (!p) return FP8W8A8_ERR_HIP;
+  p->device = device;
+  p->n = n;
+  p->k = k;
+  p->w = static_cast<const uint8_t*>(w_fp8);
+  p->w_scale = w_scale;
+  p->bias = static_cast<const uint16_t*>(bias_bf16);
+  p->cu_count = cus > 0 ? cus : 256;
+  fill_buckets(kW8A16, n, p->cu_count, p->max_m, p->config);
+  *out = p;
+  return FP8W8A8_OK;
+}
+
+int fp8_w8a16_run(const fp8_w8a16_plan* plan, int64_t m, const void* a_bf16, void* out_bf16, void* stream) {
+  if (!plan || !a_bf16 || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(a_bf16, 16) || !aligned(out_bf16, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (m == 0) return FP8W8A8_OK;
+  const int c = bucket_config(kW8A16, plan->max_m, plan->config, plan->n, m);
+  if (!grid_fits(kW8A16, c, m, plan->n)) return FP8W8A8_ERR_BAD_SHAPE;
+  hipError_t e = launch_w8a16(c, m, plan->n, plan->k, static_cast<const uint16_t*>(a_bf16), plan->w, plan->w_scale,
+                              plan->bias, static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+void fp8_w8a16_destroy(fp8_w8a16_plan* plan) { free(plan); }
+
+int fp8_w8a16_plan_config(const fp8_w8a16_plan* plan, int64_t m, int* config_id, int* tile_m, int* tile_n,
+                          int64_t* workgroups) {
+  if (!plan || !config_id || !tile_m || !tile_n || !workgroups) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  const int c = bucket_config(kW8A16, plan->max_m, plan->config, plan->n, m > 0 ? m : 1);
+  const GemmConfig* g = w8a16_config(c);
+  *config_id = c;
+  *tile_m = g->tile_m;
+  *tile_n = g->tile_n;
+  *workgroups = m > 0 ? w8a16_workgroups(c, m, plan->n) : 0;
+  return FP8W8A8_OK;
+}
+
+int fp8_w8a16_config_count(void) { return w8a16_config_count(); }
+
+int fp8_w8a16_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,
+                         const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream) {
+  if (config_id < 0 || config_id >= w8a16_config_count()) return FP8W8A8_ERR_INVALID_ARG;
+  if (!a_bf16 || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(a_bf16, 16) || !aligned(out_bf16, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (m == 0) return FP8W8A8_OK;
+  if (!grid_fits(kW8A16, config_id, m, n)) return FP8W8A8_ERR_BAD_SHAPE;
+  st = current_device_ok();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_w8a16(config_id, m, n, k, static_cast<const uint16_t*>(a_bf16),
+                              static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
+                              static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 

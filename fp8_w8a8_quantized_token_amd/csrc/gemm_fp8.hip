@@ -35,17 +35,10 @@
 //     output leaves in whole 128-byte lines (16 bytes per lane) instead of scattered
 //     8-byte pieces.
 #include "internal.h"
+#include "gemm_common.h"
 
 namespace fp8w8a8 {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer descriptor, word 3
 
 struct GemmArgs {
   const uint8_t* qa;
@@ -58,117 +51,8 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-// Raw buffer descriptor in SGPRs: 48-bit base, stride 0, num_records bytes.
-__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = kBufferConfig;
-  return r;
-}
-
-// buffer_load_dwordx4 ... lds: lane i's 16 bytes land at LDS address lds + 16 i. Issued
-// from inline asm so the compiler does not make every later LDS read wait for all
-// fills in flight; the kernel waits for exactly the fills it needs (vmcnt) and
-// synchronises the workgroup itself. The instruction has no register result.
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // v_cvt_pk_bf16_f32: round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-// Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin (id % 8);
-// renumber so XCD x owns a contiguous range of logical tiles, then walk that range in
-// groups of GROUP_M tile rows so concurrent tiles share operand panels in L2.
-template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = gridDim.x;
-  const int id = blockIdx.x;
-  const int q = nwg / kXcds, r = nwg % kXcds;
-  const int xcd = id % kXcds, local = id / kXcds;
-  const int logical = xcd * q + min(xcd, r) + local;
-  const int group_size = GROUP_M * tiles_n;
-  const int group = logical / group_size;
-  const int first_m = group * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = logical - group * group_size;
-  tm = first_m + in_group % gm;
-  tn = in_group / gm;
-}
-
-// Distinct LDS objects per (kernel, stage).
-template <typename Tag, int I, int BYTES>
-__device__ __forceinline__ uint8_t* stage_buf() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
-  return buf;
-}
-
-// s_waitcnt with vmcnt = N (0..63) and lgkmcnt = 0 (gfx9 encoding, expcnt untouched).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
-}
-
-// Wait until the fills of the stage about to be read have landed, allowing the
-// `pending` younger stages (F fills each) to stay in flight; also drains this wave's
-// LDS reads (lgkmcnt(0)) so the workgroup barrier that follows may recycle a buffer.
-template <int F, int S>
-__device__ __forceinline__ void wait_stage(int pending) {
-  if constexpr (S >= 6) {
-    if (pending >= 5) { wait_vm_lgkm0<5 * F>(); return; }
-  }
-  if constexpr (S >= 5) {
-    if (pending >= 4) { wait_vm_lgkm0<4 * F>(); return; }
-  }
-  if constexpr (S >= 4) {
-    if (pending >= 3) { wait_vm_lgkm0<3 * F>(); return; }
-  }
-  if constexpr (S >= 3) {
-    if (pending >= 2) { wait_vm_lgkm0<2 * F>(); return; }
-  }
-  if (pending >= 1) { wait_vm_lgkm0<F>(); return; }
-  wait_vm_lgkm0<0>();
-}
-
-// Interleave the MFMAs of the current sub-step with the LDS reads of the next one:
-// after each MFMA, up to R ds_reads (the matrix pipe keeps running while they issue).
-template <int MFMAS, int READS>
-__device__ __forceinline__ void interleave_mfma_ds_read() {
-  constexpr int R = (READS + MFMAS - 1) / MFMAS;
-#pragma unroll
-  for (int i = 0; i < MFMAS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if (R > 0 && (i + 1) * R <= READS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS reads
-  }
-}
-
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
 struct KernelTag {};
-
-// LDS swizzle of 16-byte chunks within a tile row of BK bytes: chunk c of row r sits at
-// position c ^ swz(r). Chosen so that 16 consecutive rows read at one logical chunk hit
-// 16 distinct 16-byte bank groups of a 256-byte LDS line, and any 8 consecutive rows 8
-// distinct groups of a 128-byte line: the ds_read_b128 operand reads are conflict free.
-template <int BK>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 64) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
-  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
-}
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {

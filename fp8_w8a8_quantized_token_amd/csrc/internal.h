@@ -46,4 +46,12 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
                        const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
                        hipStream_t stream);
 
+// The FP8 weight-only (W8A16) GEMM: out[m, n] = bf16(sum_k a[m, k] dec(qw[n, k]) * w_scale[n] + bias[n]).
+int w8a16_config_count();
+const GemmConfig* w8a16_config(int id);
+int64_t w8a16_workgroups(int id, int64_t m, int64_t n);
+int w8a16_threads(int id);
+hipError_t launch_w8a16(int id, int64_t m, int64_t n, int64_t k, const uint16_t* a, const uint8_t* qw,
+                        const float* w_scale, const uint16_t* bias, uint16_t* out, hipStream_t stream);
+
 }  // namespace fp8w8a8

@@ -208,6 +208,92 @@ class Fp8Linear:
     __call__ = forward
 
 
+class Fp8WeightOnlyLinear:
+    """An FP8 weight-only (W8A16) linear: e4m3fn weight with per-channel scales, bf16 activation.
+
+    The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
+    (longcat-avatar-compare.pages.dev, speed overview): the weight is quantised per
+    output channel once at construction (or passed in as (w_fp8, w_scale)); the
+    activation is used as it is, in bf16, and the product runs on the bf16 matrix cores.
+    """
+
+    def __init__(self, weight=None, bias=None, *, w_fp8=None, w_scale=None):
+        if weight is not None:
+            if w_fp8 is not None or w_scale is not None:
+                raise ValueError("pass either a bf16 weight or (w_fp8, w_scale), not both")
+            w_fp8, w_scale = quant_weights_per_channel(weight)
+        if w_fp8 is None or w_scale is None:
+            raise ValueError("Fp8WeightOnlyLinear needs a bf16 weight or a pre-quantised (w_fp8, w_scale)")
+        w_fp8 = _codes(w_fp8)
+        _require(w_fp8, (torch.uint8,), "w_fp8", 2)
+        _require(w_scale, (torch.float32,), "w_scale", 1)
+        n, k = w_fp8.shape
+        if w_scale.shape[0] != n:
+            raise ValueError("w_scale must have one entry per output channel")
+        if bias is not None:
+            _require(bias, (torch.bfloat16,), "bias", 1)
+            if bias.shape[0] != n:
+                raise ValueError("bias must have one entry per output channel")
+        self.w_fp8, self.w_scale, self.bias = w_fp8, w_scale, bias  # the plan borrows these
+        self.n, self.k = n, k
+        self.device = w_fp8.device
+        plan = ctypes.c_void_p()
+        check(lib().fp8_w8a16_create(self.device.index or 0, n, k, _ptr(w_fp8), _ptr(w_scale), _ptr(bias),
+                                     ctypes.byref(plan)), "fp8_w8a16_create")
+        self._plan = plan
+        self._lib = lib()
+
+    def __del__(self):
+        plan = getattr(self, "_plan", None)
+        if plan is not None and plan.value:
+            self._lib.fp8_w8a16_destroy(plan)
+            self._plan = None
+
+    def config(self, m):
+        """(config_id, tile_m, tile_n, workgroups) the plan launches for m activation rows."""
+        cid, tm, tn, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+        check(lib().fp8_w8a16_plan_config(self._plan, m, ctypes.byref(cid), ctypes.byref(tm), ctypes.byref(tn),
+                                          ctypes.byref(wg)), "fp8_w8a16_plan_config")
+        return cid.value, tm.value, tn.value, wg.value
+
+    def forward(self, x, out=None):
+        """out [..., n] bf16 from a bf16 x [..., k]."""
+        lead = x.shape[:-1]
+        if x.shape[-1] != self.k:
+            raise ValueError(f"input has {x.shape[-1]} features, the weight expects {self.k}")
+        x2 = x.reshape(-1, self.k).contiguous()
+        _require(x2, (torch.bfloat16,), "x", 2)
+        m = x2.shape[0]
+        if out is None:
+            out = torch.empty((m, self.n), dtype=torch.bfloat16, device=x2.device)
+        else:
+            _require(out, (torch.bfloat16,), "out")
+            if out.numel() != m * self.n:
+                raise ValueError("out has the wrong size")
+        check(lib().fp8_w8a16_run(self._plan, m, _ptr(x2), _ptr(out), _stream(x2)), "fp8_w8a16_run")
+        return out.reshape(*lead, self.n)
+
+    __call__ = forward
+
+
+def w8a16_config_count():
+    return lib().fp8_w8a16_config_count()
+
+
+def w8a16_run_config(config_id, a, w_fp8, w_scale, bias=None, out=None):
+    """Test hook: run W8A16 configuration `config_id` directly (every configuration is held to parity)."""
+    w_fp8 = _codes(w_fp8)
+    _require(a, (torch.bfloat16,), "a", 2)
+    _require(w_fp8, (torch.uint8,), "w_fp8", 2)
+    m, k = a.shape
+    n = w_fp8.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    check(lib().fp8_w8a16_run_config(config_id, m, n, k, _ptr(a), _ptr(w_fp8), _ptr(w_scale), _ptr(bias),
+                                     _ptr(out), _stream(a)), "fp8_w8a16_run_config")
+    return out
+
+
 def linear(a, w_fp8, w_scale, bias=None, a_scale=None):
     """One-shot FP8 linear (creates, runs and frees a plan): out [m, n] bf16."""
     return Fp8Linear(w_fp8=w_fp8, w_scale=w_scale, bias=bias).forward(a, a_scale)

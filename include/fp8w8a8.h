@@ -245,6 +245,39 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
                         const float* a_scale, const void* w_fp8, const float* w_scale,
                         const void* bias_bf16, void* out_bf16, void* stream);
 
+/* ---- FP8 weight-only linear (W8A16) --------------------------------------------
+ *
+ * The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
+ * (longcat-avatar-compare.pages.dev, speed overview table): the weight is stored as
+ * e4m3fn codes with per-output-channel scales (fp8_quant_weights_per_channel), the
+ * activation stays bf16 and is not quantised:
+ *
+ *   out[m,n] = bf16_rne( fl32( sum_k a[m,k] * dec(qW[n,k]) ) * sW[n] + bias[n] )
+ *
+ * The product runs on the bf16 matrix cores (every e4m3fn value is exact in bf16)
+ * with fp32 accumulation; the epilogue runs in fp32 and rounds once. Layouts,
+ * ownership, streams and errors are as for fp8_linear_*: a [m, k] bf16 and out
+ * [m, n] bf16 row-major, 16-byte aligned; the plan borrows qW [n, k], sW [n] and
+ * bias [n] (or NULL), with the same shape and alignment rules as fp8_linear_create.
+ * No workspace is needed.
+ */
+typedef struct fp8_w8a16_plan fp8_w8a16_plan;
+
+int fp8_w8a16_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+                     const void* bias_bf16, fp8_w8a16_plan** out);
+
+/* m == 0 is a no-op. a_bf16 and out_bf16 are device pointers, 16-byte aligned. */
+int fp8_w8a16_run(const fp8_w8a16_plan* plan, int64_t m, const void* a_bf16, void* out_bf16, void* stream);
+
+void fp8_w8a16_destroy(fp8_w8a16_plan* plan);
+
+/* Introspection and the test hook, as fp8_linear_plan_config / fp8_gemm_*. */
+int fp8_w8a16_plan_config(const fp8_w8a16_plan* plan, int64_t m, int* config_id, int* tile_m, int* tile_n,
+                          int64_t* workgroups);
+int fp8_w8a16_config_count(void);
+int fp8_w8a16_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,
+                         const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

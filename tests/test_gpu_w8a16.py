@@ -1,0 +1,122 @@
+"""GPU parity of the FP8 weight-only linear (W8A16) against the float64 oracle.
+
+The weight is quantised per output channel by the library (and checked bit for bit
+against the oracle's quantiser); the activation stays bf16. Outputs are compared
+with the unrounded float64 reference: |gpu - ref| <= 1e-2 (|ref| + 1) elementwise and
+relative Frobenius error <= 2e-3. Covered: the tiny shape in full; every compiled
+configuration on ragged m / n / k tails; every finite e4m3fn code through the
+in-register fp8 -> bf16 conversion (bit exact); A = 0 (output == bias exactly); no
+bias; the selector; full-size FFN shapes on sampled rows.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_quantized_token_amd as fp8
+from oracle import e4m3, quant as oq, w8a16 as ow
+from tests._helpers import assert_linear_close, require_gpu, sample_rows
+from workloads import bf16_bits, make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+try:
+    N_CONFIGS = fp8.w8a16_config_count()
+except Exception:  # library not built: the tests below report it
+    N_CONFIGS = 1
+
+TAIL_SHAPES = [(1, 16, 16), (26, 144, 48), (63, 16, 272), (65, 144, 16), (257, 144, 272), (300, 272, 400),
+               (513, 528, 1040)]
+
+
+def _ref(case, qw=None, sw=None):
+    if qw is None:
+        qw, sw = oq.quant_weights_per_channel(bf16_bits(case.w))
+    b = None if case.bias is None else bf16_bits(case.bias)
+    return ow.w8a16_ref(bf16_bits(case.a), qw, sw, b), qw, sw
+
+
+def test_tiny_full_and_weight_codes():
+    dev = require_gpu()
+    cfg = make_config("tiny")
+    a, w, b = cfg["activations"]["a"], cfg["weights"]["linear"], cfg["biases"]["linear"]
+    lin = fp8.Fp8WeightOnlyLinear(w.to(dev), b.to(dev))
+    out = lin(a.to(dev))
+    torch.cuda.synchronize()
+    qw, sw = oq.quant_weights_per_channel(bf16_bits(w))
+    assert np.array_equal(lin.w_fp8.cpu().numpy(), qw) and np.array_equal(lin.w_scale.cpu().numpy(), sw)
+    assert_linear_close(out, ow.w8a16_ref(bf16_bits(a), qw, sw, bf16_bits(b)), "w8a16 tiny")
+
+
+@pytest.mark.parametrize("config", range(N_CONFIGS))
+@pytest.mark.parametrize("m,n,k", TAIL_SHAPES)
+def test_every_config_on_ragged_tails(config, m, n, k):
+    dev = require_gpu()
+    case = make_case(m, n, k, seed=m + 3 * n + 7 * k, kind="normal")
+    ref, qw, sw = _ref(case)
+    out = fp8.w8a16_run_config(config, case.a.to(dev), torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev),
+                               case.bias.to(dev))
+    assert_linear_close(out, ref, f"w8a16 config {config} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("config", range(N_CONFIGS))
+def test_every_e4m3_code_through_the_conversion(config):
+    # one-hot activation rows pick single weight codes: out[t, n] = dec(qw[n, t]) exactly
+    dev = require_gpu()
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)  # 254 finite codes
+    k = 256
+    n = 64
+    rng = np.random.default_rng(config)
+    qw = np.empty((n, k), np.uint8)
+    for r in range(n):
+        qw[r, :254] = rng.permutation(codes)
+        qw[r, 254:] = 0
+    a = torch.eye(k, dtype=torch.bfloat16)[:200]  # rows 0..199
+    sw = np.ones(n, np.float32)
+    out = fp8.w8a16_run_config(config, a.to(dev), torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+    got = out.float().cpu().numpy()
+    exp = e4m3.decode(qw[:, :200]).T  # e4m3 values are exact in bf16
+    assert np.array_equal(got, exp.astype(np.float32))
+
+
+def test_zero_activation_gives_bias_and_no_bias():
+    dev = require_gpu()
+    case = make_case(70, 272, 528, seed=8, kind="normal")
+    lin = fp8.Fp8WeightOnlyLinear(case.w.to(dev), case.bias.to(dev))
+    zero = torch.zeros((70, 528), dtype=torch.bfloat16, device=dev)
+    out = lin(zero)
+    assert torch.equal(out, case.bias.to(dev).expand(70, -1))
+    nob = fp8.Fp8WeightOnlyLinear(case.w.to(dev))
+    ref, _, _ = _ref(dataclasses.replace(case, bias=None))
+    assert_linear_close(nob(case.a.to(dev)), ref, "w8a16 no bias")
+
+
+def test_selector_and_3d_input():
+    dev = require_gpu()
+    case = make_case(96, 400, 272, seed=9, kind="normal")
+    lin = fp8.Fp8WeightOnlyLinear(case.w.to(dev), case.bias.to(dev))
+    for m in (1, 26, 64, 300, 4096, 32760):
+        cid, tm, tn, wg = lin.config(m)
+        assert 0 <= cid < N_CONFIGS and wg == -(-m // tm) * -(-400 // tn)
+    out = lin(case.a.to(dev).reshape(4, 24, 272))
+    assert out.shape == (4, 24, 400)
+    ref, _, _ = _ref(case)
+    assert_linear_close(out.reshape(96, 400), ref, "w8a16 3-d input")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["ffn_up", "ffn_down"])
+def test_ffn_full_size_sampled_rows(name):
+    dev = require_gpu()
+    cfg = make_config(name)
+    a = cfg["activations"]["a"]
+    w, b = cfg["weights"][name], cfg["biases"][name]
+    lin = fp8.Fp8WeightOnlyLinear(w.to(dev), b.to(dev))
+    out = lin(a.to(dev)).cpu()
+    qw, sw = oq.quant_weights_per_channel(bf16_bits(w))
+    assert np.array_equal(lin.w_fp8.cpu().numpy(), qw)
+    rows = sample_rows(a.shape[0])
+    ref = ow.w8a16_ref(bf16_bits(a)[rows], qw, sw, bf16_bits(b))
+    assert_linear_close(out[rows], ref, f"w8a16 {name} sampled rows")
