@@ -17,6 +17,10 @@ dominant launch): a second region of K steps records HIP events on the launch
 stream around every launch, giving each kernel's average launch duration.
 `cpu_baseline` times the CPU oracle (numpy, float64) on the same workload.
 
+`w8a16` (outside the step) times the FP8 weight-only linear (bf16 activation x
+per-channel e4m3fn weight on the bf16 matrix cores) on the same FFN-up shape, against
+the dense bf16 MFMA peak.
+
 `producer` (outside the step) times the activation producer that feeds the
 FFN-down linear: GELU (tanh form) of the FFN-up output followed by per-token
 e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
@@ -40,6 +44,7 @@ METRIC = "FP8 W8A8 linear TFLOP/s (quant+GEMM+epilogue), M4096 N8192 K2048; quan
 M, N, K = 4096, 8192, 2048
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_ffn_up_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", "gemm_fp8.hip")
 
@@ -132,6 +137,46 @@ def copy_calibration(torch, dev):
     del src, dst
 
 
+def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
+    """FP8 weight-only linear on the FFN-up shape: per-launch events on the launch stream."""
+    from workloads.synth import activation, bias as gen_bias, weight
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    sets = []
+    for i in range(nsets):
+        a = activation(0, 2, 60 + i, M, K, "normal").to(dev)
+        lin = fp8.Fp8WeightOnlyLinear(weight(0, 2, 160 + i, N, K).to(dev), gen_bias(0, 2, 260 + i, N).to(dev))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sets.append((a, lin, out))
+    torch.cuda.synchronize()
+
+    def run(i):
+        a, lin, out = sets[i % nsets]
+        st = lib.fp8_w8a16_run(lin._plan, M, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(out.data_ptr()), sptr)
+        if st:
+            from fp8_w8a8_quantized_token_amd import _lib
+            raise _lib.Fp8W8A8Error(st, "fp8_w8a16_run")
+
+    for i in range(5):
+        run(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        run(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    avg = sum(ts) / len(ts)
+    tflops = 2.0 * M * N * K / (avg * 1e-3) / 1e12
+    cid, tm, tn, wg = sets[0][1].config(M)
+    del sets
+    torch.cuda.empty_cache()
+    return {"kernel": "gemm_w8a16_kernel", "M": M, "N": N, "K": K, "avg_launch_us": round(avg * 1e3, 3),
+            "median_launch_us": round(ts[len(ts) // 2] * 1e3, 3), "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "bound": "mfma", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "config": {"id": cid, "tile_m": tm, "tile_n": tn, "workgroups": wg}}
+
+
 def cpu_baseline(budget_s=20.0):
     """The CPU oracle (as it stands) on the FFN-up workload: quant + exact float64 linear."""
     import numpy as np
@@ -180,6 +225,7 @@ def main():
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
+    ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
     ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
                     help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,9 +366,11 @@ def main():
         },
         "gemm_median_us": round(gemm_ms[len(gemm_ms) // 2] * 1e3, 3),
     }
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_w8a16:
+        result["w8a16"] = w8a16_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if not args.no_producer:
-        del sets
-        torch.cuda.empty_cache()
         result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if args.copy_calibration:
         copy_calibration(torch, dev)
