@@ -18,6 +18,8 @@ Modules
   linear  exact float64 FP8 product and the scale/bias epilogue
   act     GELU / SiLU rounded exactly to bf16 (the producer upstream of the FFN-down
           linear), then the per-token quantiser: the fused producer's result
+  e5m2    decode / round-to-nearest-even saturating encode of OCP e5m2 codes
+  tensor_quant  per-tensor quantisation (either format) and fp32 dequantisation
   w8a16   the FP8 weight-only linear: bf16 activation times the per-channel e4m3fn
           weight, in float64
 
@@ -26,6 +28,6 @@ outside this package (the format definition, torch's CPU float8 cast, brute
 force, closed forms and invariants); nothing here is "parity unpinned".
 """
 
-from . import e4m3, quant, linear, act, w8a16  # noqa: F401
+from . import e4m3, e5m2, quant, linear, act, w8a16, tensor_quant  # noqa: F401
 
-__all__ = ["e4m3", "quant", "linear", "act", "w8a16"]
+__all__ = ["e4m3", "e5m2", "quant", "linear", "act", "w8a16", "tensor_quant"]

@@ -8,11 +8,15 @@ import pytest
 
 import oracle.act as act_mod
 import oracle.e4m3 as e4m3_mod
+import oracle.e5m2 as e5m2_mod
+import oracle.tensor_quant as tq_mod
 import oracle.linear as linear_mod
 import oracle.quant as quant_mod
 import oracle.w8a16 as w8a16_mod
 from tests import test_oracle_act as ta
 from tests import test_oracle_e4m3 as te
+from tests import test_oracle_e5m2 as t5
+from tests import test_oracle_tensor_quant as ttq
 from tests import test_oracle_linear as tl
 from tests import test_oracle_quant as tq
 from tests import test_oracle_w8a16 as tw
@@ -222,3 +226,38 @@ def test_w8a16_dropped_scale_is_caught(monkeypatch):
     monkeypatch.setattr(w8a16_mod, "w8a16_ref",
                         lambda a, qw, sw, b=None: real(a, qw, np.ones_like(np.asarray(sw, np.float32)), b))
     _fails(tw.test_equals_w8a8_where_the_activation_quant_is_the_identity)
+
+
+# --- e5m2 codes and the per-tensor quantiser
+
+
+def test_e5m2_wrong_bias_is_caught(monkeypatch):
+    real = e5m2_mod.decode
+    monkeypatch.setattr(e5m2_mod, "decode", lambda c: real(c) * 0.5)  # as if the exponent bias were 16
+    _fails(t5.test_decode_landmarks, GOLDEN)
+
+
+def test_e5m2_half_up_is_caught(monkeypatch):
+    def encode_half_up(values):
+        v = np.asarray(values, np.float32).astype(np.float64)
+        neg = np.signbit(v)
+        a = np.minimum(np.abs(v), 57344.0)
+        sub = np.floor(a * 2.0 ** 16 + 0.5)
+        safe = np.where(a >= 2.0 ** -14, a, 1.0)
+        _, e = np.frexp(safe)
+        e = e.astype(np.int64) - 1
+        m = np.floor((safe / np.exp2(e.astype(np.float64)) - 1.0) * 4.0 + 0.5).astype(np.int64)
+        e = np.where(m == 4, e + 1, e)
+        m = np.where(m == 4, 0, m)
+        code = np.where(a < 2.0 ** -14, sub.astype(np.int64), ((e + 15) << 2) | m)
+        return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+    monkeypatch.setattr(e5m2_mod, "encode", encode_half_up)
+    _fails(t5.test_encode_matches_brute_force_at_every_boundary)
+
+
+def test_per_row_scale_in_the_tensor_quantiser_is_caught(monkeypatch):
+    def per_row(x_bits, fmt):
+        q, s = quant_mod.quant_rows(np.atleast_2d(np.asarray(x_bits, np.uint16)))
+        return q.reshape(np.shape(x_bits)), s[0]
+    monkeypatch.setattr(tq_mod, "quant_tensor", per_row)
+    _fails(ttq.test_worked_tensor_power_of_two_scale)
