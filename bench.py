@@ -21,6 +21,10 @@ stream around every launch, giving each kernel's average launch duration.
 per-channel e4m3fn weight on the bf16 matrix cores) on the same FFN-up shape, against
 the dense bf16 MFMA peak.
 
+`tensor_quant` (outside the step) times the per-tensor state-dict conversion (one
+scale per tensor, e4m3fn and e5m2) of the FFN-up weight [8192, 2048] and of the DiT
+FFN-down input size [32760, 8192]: an amax pass and a quantise pass over HBM.
+
 `producer` (outside the step) times the activation producer that feeds the
 FFN-down linear: GELU (tanh form) of the FFN-up output followed by per-token
 e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
@@ -177,6 +181,44 @@ def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
             "config": {"id": cid, "tile_m": tm, "tile_n": tn, "workgroups": wg}}
 
 
+def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
+    """Per-tensor quantisation (both formats): two launches, HBM-resident rotating inputs."""
+    from fp8_w8a8_quantized_token_amd import _lib
+    from workloads.synth import activation
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    ws = torch.empty((lib.fp8_quant_tensor_workspace_bytes(),), dtype=torch.uint8, device=dev)
+    scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    out = {"bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s", "shapes": []}
+    for rows, cols, nsets in ((8192, 2048, 16), (32760, 8192, 2)):
+        xs = [activation(0, 5, 80 + i, rows, cols, "normal").to(dev) for i in range(nsets)]
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        for fmt_name, fmt in (("e4m3fn", _lib.FMT_E4M3FN), ("e5m2", _lib.FMT_E5M2)):
+            def run(i):
+                st = lib.fp8_quant_tensor(ctypes.c_void_p(xs[i % nsets].data_ptr()), rows * cols, fmt,
+                                          ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(scale.data_ptr()),
+                                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr)
+                if st:
+                    raise _lib.Fp8W8A8Error(st, "fp8_quant_tensor")
+            for i in range(3):
+                run(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                run(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            algo = 3 * rows * cols + 4
+            out["shapes"].append({"rows": rows, "cols": cols, "format": fmt_name, "us": round(us, 2),
+                                  "algorithmic_bytes": algo, "achieved": round(algo / (us * 1e-6) / 1e9, 1),
+                                  "hbm_bytes_two_pass": 5 * rows * cols + 4,
+                                  "frac": round(algo / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+        del xs, q
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(budget_s=20.0):
     """The CPU oracle (as it stands) on the FFN-up workload: quant + exact float64 linear."""
     import numpy as np
@@ -226,6 +268,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
     ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
+    ap.add_argument("--no-tensor-quant", action="store_true", help="skip the per-tensor quantisation timing")
     ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
                     help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -372,6 +415,8 @@ def main():
         result["w8a16"] = w8a16_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if not args.no_producer:
         result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
+    if not args.no_tensor_quant:
+        result["tensor_quant"] = tensor_quant_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 50)))
     if args.copy_calibration:
         copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}

@@ -16,6 +16,8 @@ from .ops import (  # noqa: F401
     act_quant_rows,
     act_rows,
     act_table,
+    dequant_tensor,
+    quant_tensor,
     gemm_config_count,
     gemm_run_config,
     linear,
@@ -35,6 +37,8 @@ __all__ = [
     "act_table",
     "act_rows",
     "act_quant_rows",
+    "quant_tensor",
+    "dequant_tensor",
     "linear",
     "quant_rows",
     "quant_weights_per_channel",

@@ -27,6 +27,9 @@ ACT_GELU_TANH = 2
 ACT_SILU = 3
 ACT_TABLE_BYTES = 131072
 
+FMT_E4M3FN = 0
+FMT_E5M2 = 1
+
 MAX_ROWS = 1 << 24
 MAX_DIM = 1 << 20
 
@@ -39,6 +42,9 @@ SIGNATURES = {
     "fp8_quant_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_quant_weights_per_channel": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_act_table_build": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p]),
+    "fp8_quant_tensor_workspace_bytes": (ctypes.c_size_t, []),
+    "fp8_quant_tensor": (ctypes.c_int, [_c_p, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_dequant_tensor": (ctypes.c_int, [_c_p, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]),
     "fp8_act_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_act_quant_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "fp8_linear_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.POINTER(_c_p)]),

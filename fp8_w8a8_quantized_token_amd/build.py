@@ -20,7 +20,7 @@ LIB_NAME = "libfp8w8a8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quant_rows.hip", "act_quant.hip", "gemm_fp8.hip", "gemm_w8a16.hip"]
+SOURCES = ["api.hip", "quant_rows.hip", "act_quant.hip", "quant_tensor.hip", "gemm_fp8.hip", "gemm_w8a16.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",

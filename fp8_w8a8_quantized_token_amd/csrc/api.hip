@@ -243,6 +243,46 @@ int fp8_act_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, const voi
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 
+size_t fp8_quant_tensor_workspace_bytes(void) { return quant_tensor_workspace_bytes(); }
+
+static int check_tensor_args(const void* x, int64_t numel, int format, const void* out) {
+  if (!x || !out) return FP8W8A8_ERR_INVALID_ARG;
+  if (format != FP8W8A8_FMT_E4M3FN && format != FP8W8A8_FMT_E5M2) return FP8W8A8_ERR_INVALID_ARG;
+  if (numel < 0 || numel >= FP8W8A8_MAX_ROWS * FP8W8A8_MAX_DIM || numel % 16 != 0) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(x, 16) || !aligned(out, 16)) return FP8W8A8_ERR_MISALIGNED;
+  return FP8W8A8_OK;
+}
+
+int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_tensor_args(x_bf16, numel, format, q_out);
+  if (st != FP8W8A8_OK) return st;
+  if (!scale_out || !workspace) return FP8W8A8_ERR_INVALID_ARG;
+  if (!aligned(scale_out, 4) || !aligned(workspace, 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < quant_tensor_workspace_bytes()) return FP8W8A8_ERR_WORKSPACE_TOO_SMALL;
+  if (numel == 0) return FP8W8A8_OK;
+  int cus = 0;
+  st = current_device_ok(&cus);
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_quant_tensor(static_cast<const uint16_t*>(x_bf16), numel, format, static_cast<uint8_t*>(q_out),
+                                     scale_out, static_cast<float*>(workspace), cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* scale, float* out_f32, void* stream) {
+  int st = check_tensor_args(q, numel, format, out_f32);
+  if (st != FP8W8A8_OK) return st;
+  if (!scale) return FP8W8A8_ERR_INVALID_ARG;
+  if (!aligned(scale, 4)) return FP8W8A8_ERR_MISALIGNED;
+  if (numel == 0) return FP8W8A8_OK;
+  int cus = 0;
+  st = current_device_ok(&cus);
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = launch_dequant_tensor(static_cast<const uint8_t*>(q), numel, format, scale, out_f32, cus,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
 int fp8_quant_weights_per_channel(const void* w_bf16, int64_t n, int64_t k, void* w_fp8_out,
                                   float* w_scale_out, void* stream) {
   if (n == 0 || k == 0) return FP8W8A8_ERR_BAD_SHAPE;

@@ -24,6 +24,14 @@ hipError_t launch_act_rows(const uint16_t* x, int64_t elems, const uint16_t* tab
 hipError_t launch_act_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* table, uint8_t* q,
                                  float* scale, int cus, hipStream_t stream);
 
+// Per-tensor quantisation (amax partials into `workspace`, then the codes and the scale)
+// and fp32 dequantisation; numel % 16 == 0, 16-byte aligned buffers.
+size_t quant_tensor_workspace_bytes();
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t numel, int fmt, uint8_t* q, float* scale, float* workspace,
+                               int cus, hipStream_t stream);
+hipError_t launch_dequant_tensor(const uint8_t* q, int64_t numel, int fmt, const float* scale, float* out, int cus,
+                                 hipStream_t stream);
+
 // One compiled GEMM kernel configuration.
 struct GemmConfig {
   int id;

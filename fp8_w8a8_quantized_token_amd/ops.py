@@ -12,7 +12,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import A_BF16, A_E4M3, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU, ACT_TABLE_BYTES, check, lib
+from ._lib import (A_BF16, A_E4M3, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU, ACT_TABLE_BYTES, FMT_E4M3FN, FMT_E5M2,
+                   check, lib)
 
 ACTIVATIONS = {"gelu_erf": ACT_GELU_ERF, "gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
 
@@ -117,6 +118,44 @@ def act_quant_rows(x, table, q=None, scale=None):
     check(lib().fp8_act_quant_rows(_ptr(x2), m, k, _ptr(table), _ptr(q), _ptr(s), _stream(x2)),
           "fp8_act_quant_rows")
     return q, s
+
+
+FORMATS = {"e4m3fn": FMT_E4M3FN, "e5m2": FMT_E5M2}
+
+
+def quant_tensor(x, fmt="e4m3fn", workspace=None):
+    """Per-tensor quantisation of a bf16 tensor -> (codes uint8 of x's shape, scale fp32 [1]).
+
+    One scale for the whole tensor, s = amax / fmax (448 for e4m3fn, 57344 for e5m2):
+    the state-dict conversion of the QuantizeFP8Format page. numel must be a multiple of 16.
+    """
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
+    xc = x.contiguous()
+    _require(xc, (torch.bfloat16,), "x")
+    q = torch.empty(xc.shape, dtype=torch.uint8, device=xc.device)
+    s = torch.empty((1,), dtype=torch.float32, device=xc.device)
+    ws_bytes = lib().fp8_quant_tensor_workspace_bytes()
+    if workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xc.device)
+    check(lib().fp8_quant_tensor(_ptr(xc), xc.numel(), FORMATS[fmt], _ptr(q), _ptr(s), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(xc)), "fp8_quant_tensor")
+    return q, s
+
+
+def dequant_tensor(q, scale, fmt="e4m3fn"):
+    """fp32 values dec(q) * scale of a per-tensor quantised tensor (q uint8 or float8, scale fp32 [1])."""
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
+    qc = q.contiguous()
+    if qc.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        qc = qc.view(torch.uint8)
+    _require(qc, (torch.uint8,), "q")
+    _require(scale, (torch.float32,), "scale")
+    out = torch.empty(qc.shape, dtype=torch.float32, device=qc.device)
+    check(lib().fp8_dequant_tensor(_ptr(qc), qc.numel(), FORMATS[fmt], _ptr(scale), _ptr(out), _stream(qc)),
+          "fp8_dequant_tensor")
+    return out
 
 
 class Fp8Linear:

@@ -245,6 +245,39 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
                         const float* a_scale, const void* w_fp8, const float* w_scale,
                         const void* bias_bf16, void* out_bf16, void* stream);
 
+/* ---- per-tensor FP8 quantisation (state-dict conversion) -------------------------
+ *
+ * The QuantizeFP8Format page (runcomfy.com, "Quantize Model to FP8 Format")
+ * converts each tensor to float8_e4m3fn or float8_e5m2 with "a simple scaling
+ * technique"; the Stable Diffusion 3.5 FP8 page (dn008.com.cn, section on FP8,
+ * steps 1-4) gives the steps. One scale per tensor, fmax = 448 or 57344:
+ *
+ *   s   = fl32(amax / fmax)            (0 for an all-zero tensor)
+ *   q   = rne_sat(fl32(x / s))         (signed-zero codes when s == 0)
+ *   x'  = fl32(dec(q) * s)             (fp8_dequant_tensor)
+ *
+ * e5m2 is the OCP E5M2 encoding (bias 15, largest finite 57344, saturating; the
+ * infinity and NaN codes are never produced for finite input).
+ *
+ *   x_bf16     device, bf16, numel elements (any shape, flattened), 16-byte aligned
+ *   numel      0 <= numel < FP8W8A8_MAX_ROWS * FP8W8A8_MAX_DIM, numel % 16 == 0 (0 is a no-op)
+ *   format     FP8W8A8_FMT_E4M3FN or FP8W8A8_FMT_E5M2 (else FP8W8A8_ERR_INVALID_ARG)
+ *   q_out      device, u8 codes [numel], 16-byte aligned, written
+ *   scale_out  device, one fp32, 4-byte aligned, written
+ *   workspace  device, fp8_quant_tensor_workspace_bytes() bytes, 16-byte aligned, scratch
+ *              (per-workgroup maxima); its contents need no initialisation
+ * Two launches on `stream`. Inputs must be finite.
+ */
+#define FP8W8A8_FMT_E4M3FN 0
+#define FP8W8A8_FMT_E5M2 1
+
+size_t fp8_quant_tensor_workspace_bytes(void);
+int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* out_f32[i] = fl32(dec(q[i]) * *scale). q 16-byte aligned, out_f32 16-byte aligned, scale device fp32. */
+int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* scale, float* out_f32, void* stream);
+
 /* ---- FP8 weight-only linear (W8A16) --------------------------------------------
  *
  * The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page

@@ -184,3 +184,26 @@ def test_w8a16_validation(lib):
     assert lib.fp8_w8a16_run_config(0, 4, 16, 24, A, A, A, None, A, None) == _lib.ERR_BAD_SHAPE
     assert lib.fp8_w8a16_run_config(0, 4, 16, 16, MIS16, A, A, None, A, None) == _lib.ERR_MISALIGNED
     assert lib.fp8_w8a16_run_config(0, 0, 16, 16, A, A, A, None, A, None) == _lib.OK
+
+
+def test_tensor_quant_validation(lib):
+    A = ALIGNED
+    ws = lib.fp8_quant_tensor_workspace_bytes()
+    assert ws >= 16
+    f = lib.fp8_quant_tensor
+    assert f(None, 16, 0, A, A, A, ws, None) == _lib.ERR_INVALID_ARG
+    assert f(A, 16, 2, A, A, A, ws, None) == _lib.ERR_INVALID_ARG
+    assert f(A, 16, 0, A, None, A, ws, None) == _lib.ERR_INVALID_ARG
+    assert f(A, 16, 0, A, A, None, ws, None) == _lib.ERR_INVALID_ARG
+    for numel in (8, 24, -16):
+        assert f(A, numel, 0, A, A, A, ws, None) == _lib.ERR_BAD_SHAPE, numel
+    assert f(MIS16, 16, 1, A, A, A, ws, None) == _lib.ERR_MISALIGNED
+    assert f(A, 16, 1, A, MIS4 + 1, A, ws, None) == _lib.ERR_MISALIGNED
+    assert f(A, 16, 1, A, A, A, ws - 4, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert f(A, 0, 1, A, A, A, ws, None) == _lib.OK
+    d = lib.fp8_dequant_tensor
+    assert d(A, 16, 5, A, A, None) == _lib.ERR_INVALID_ARG
+    assert d(A, 16, 0, None, A, None) == _lib.ERR_INVALID_ARG
+    assert d(A, 20, 0, A, A, None) == _lib.ERR_BAD_SHAPE
+    assert d(A, 16, 0, A, MIS16, None) == _lib.ERR_MISALIGNED
+    assert d(A, 0, 0, A, A, None) == _lib.OK
