@@ -57,15 +57,16 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(_c_i64)]),
     "fp8_gemm_config_count": (ctypes.c_int, []),
-    "fp8_w8a16_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.POINTER(_c_p)]),
+    "fp8_w8a16_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p,
+                                         ctypes.POINTER(_c_p)]),
     "fp8_w8a16_run": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_w8a16_destroy": (None, [_c_p]),
     "fp8_w8a16_plan_config": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(ctypes.c_int),
                                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                              ctypes.POINTER(_c_i64)]),
     "fp8_w8a16_config_count": (ctypes.c_int, []),
-    "fp8_w8a16_run_config": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
-                                            _c_p]),
+    "fp8_w8a16_run_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                            _c_p, _c_p, _c_p]),
     "fp8_gemm_run_config": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                            _c_p, _c_p]),
 }

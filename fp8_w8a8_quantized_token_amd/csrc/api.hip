@@ -32,6 +32,7 @@ struct fp8_linear_plan {
 
 struct fp8_w8a16_plan {
   int device;
+  int w_format;
   int64_t n, k;
   const uint8_t* w;
   const float* w_scale;
@@ -404,9 +405,10 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 
-int fp8_w8a16_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+int fp8_w8a16_create(int device, int64_t n, int64_t k, int w_format, const void* w_fp8, const float* w_scale,
                      const void* bias_bf16, fp8_w8a16_plan** out) {
   if (!out) return FP8W8A8_ERR_INVALID_ARG;
+  if (w_format != FP8W8A8_FMT_E4M3FN && w_format != FP8W8A8_FMT_E5M2) return FP8W8A8_ERR_INVALID_ARG;
   int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
   if (st != FP8W8A8_OK) return st;
   int cus = 0;
@@ -415,6 +417,7 @@ int fp8_w8a16_create(int device, int64_t n, int64_t k, const void* w_fp8, const 
   fp8_w8a16_plan* p = static_cast<fp8_w8a16_plan*>(calloc(1, sizeof(fp8_w8a16_plan)));
   if (!p) return FP8W8A8_ERR_HIP;
   p->device = device;
+  p->w_format = w_format;
   p->n = n;
   p->k = k;
   p->w = static_cast<const uint8_t*>(w_fp8);
@@ -433,7 +436,8 @@ int fp8_w8a16_run(const fp8_w8a16_plan* plan, int64_t m, const void* a_bf16, voi
   if (m == 0) return FP8W8A8_OK;
   const int c = bucket_config(kW8A16, plan->max_m, plan->config, plan->n, m);
   if (!grid_fits(kW8A16, c, m, plan->n)) return FP8W8A8_ERR_BAD_SHAPE;
-  hipError_t e = launch_w8a16(c, m, plan->n, plan->k, static_cast<const uint16_t*>(a_bf16), plan->w, plan->w_scale,
+  hipError_t e = launch_w8a16(c, plan->w_format, m, plan->n, plan->k, static_cast<const uint16_t*>(a_bf16), plan->w,
+                              plan->w_scale,
                               plan->bias, static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
@@ -455,9 +459,10 @@ int fp8_w8a16_plan_config(const fp8_w8a16_plan* plan, int64_t m, int* config_id,
 
 int fp8_w8a16_config_count(void) { return w8a16_config_count(); }
 
-int fp8_w8a16_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,
-                         const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream) {
+int fp8_w8a16_run_config(int config_id, int w_format, int64_t m, int64_t n, int64_t k, const void* a_bf16,
+                         const void* w_fp8, const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream) {
   if (config_id < 0 || config_id >= w8a16_config_count()) return FP8W8A8_ERR_INVALID_ARG;
+  if (w_format != FP8W8A8_FMT_E4M3FN && w_format != FP8W8A8_FMT_E5M2) return FP8W8A8_ERR_INVALID_ARG;
   if (!a_bf16 || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
   int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
   if (st != FP8W8A8_OK) return st;
@@ -467,7 +472,7 @@ int fp8_w8a16_run_config(int config_id, int64_t m, int64_t n, int64_t k, const v
   if (!grid_fits(kW8A16, config_id, m, n)) return FP8W8A8_ERR_BAD_SHAPE;
   st = current_device_ok();
   if (st != FP8W8A8_OK) return st;
-  hipError_t e = launch_w8a16(config_id, m, n, k, static_cast<const uint16_t*>(a_bf16),
+  hipError_t e = launch_w8a16(config_id, w_format, m, n, k, static_cast<const uint16_t*>(a_bf16),
                               static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
                               static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;

@@ -1,4 +1,4 @@
-// FP8 weight-only linear (W8A16) for gfx950: bf16 activation x e4m3fn weight.
+// FP8 weight-only linear (W8A16) for gfx950: bf16 activation x e4m3fn (or e5m2) weight.
 //
 //   out[m, n] = bf16_rne( acc[m, n] * w_scale[n] + bias[n] ),
 //   acc[m, n] = sum_k a[m, k] * dec(qw[n, k])   (fp32 accumulation on the MFMA units)
@@ -12,9 +12,11 @@
 //
 // The kernel is the FP8 GEMM's design with a bf16 left operand:
 //   * V_MFMA_F32_32X32X16_BF16. Every e4m3fn value is exact in bf16 (3 mantissa bits,
-//     exponents 2^-9 .. 2^8), so the weight fragments are converted in registers with
-//     v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact) right before the MFMAs; the LDS
-//     holds the weight as FP8 (half the bytes of a bf16 copy).
+//     exponents 2^-9 .. 2^8), and so is every finite e5m2 value (2 mantissa bits,
+//     2^-16 .. 57344), so the weight fragments are converted in registers with
+//     v_cvt_scalef32_pk_bf16_{fp8,bf8} at scale 1 (exact) right before the MFMAs; the
+//     LDS holds the weight as FP8 (half the bytes of a bf16 copy). The e5m2 weights are
+//     the QuantizeFP8Format page's default format (runcomfy.com, input parameters).
 //   * A stage holds 64 k elements: 128-byte activation rows and 64-byte weight rows,
 //     filled by buffer_load_dwordx4 ... lds, each row's 16-byte chunks swizzled so the
 //     operand reads (ds_read_b128 for the activation, ds_read_b64 for the weight) and
@@ -40,21 +42,32 @@ struct W16Args {
   int tiles_m, tiles_n;
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, int FMT>
 struct W16Tag {};
 
-// 8 e4m3fn codes (two dwords) -> 8 bf16, exactly.
+// 2 codes (one 16-bit half of a dword) -> 2 bf16, exactly (scale 1; every e4m3fn and
+// every finite e5m2 value is a bf16 value).
+template <int FMT, bool HI>
+__device__ __forceinline__ v2bf cvt2(uint32_t w) {
+  if constexpr (FMT == FP8W8A8_FMT_E5M2)
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+// 8 codes (two dwords) -> 8 bf16.
+template <int FMT>
 __device__ __forceinline__ v8bf fp8x8_to_bf16(uint2 w) {
-  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
-  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
-  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
-  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  const v2bf p0 = cvt2<FMT, false>(w.x);
+  const v2bf p1 = cvt2<FMT, true>(w.x);
+  const v2bf p2 = cvt2<FMT, false>(w.y);
+  const v2bf p3 = cvt2<FMT, true>(w.y);
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GROUP_M, int FMT>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Args args) {
-  using Tag = W16Tag<BM, BN, WAVES_M, WAVES_N, STAGES, GROUP_M>;
+  using Tag = W16Tag<BM, BN, WAVES_M, WAVES_N, STAGES, GROUP_M, FMT>;
   constexpr int KE = 64;               // k elements per stage
   constexpr int kARow = 2 * KE;        // activation row bytes per stage (bf16)
   constexpr int kWRow = KE;            // weight row bytes per stage (e4m3fn)
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   auto mfma_all = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const v8bf w = fp8x8_to_bf16(f.w[i]);
+      const v8bf w = fp8x8_to_bf16<FMT>(f.w[i]);
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, f.a[j], acc[i][j], 0, 0, 0);
     }
@@ -293,13 +306,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   }
 }
 
-template <int BM, int BN, int WM, int WN, int S, int GM>
+template <int BM, int BN, int WM, int WN, int S, int GM, int FMT>
 hipError_t launch(const W16Args& a, hipStream_t stream) {
   W16Args args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
   const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_w8a16_kernel<BM, BN, WM, WN, S, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+  gemm_w8a16_kernel<BM, BN, WM, WN, S, GM, FMT><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -330,17 +343,23 @@ int w8a16_threads(int id) {
   return c ? 64 * c->waves : 0;
 }
 
-hipError_t launch_w8a16(int id, int64_t m, int64_t n, int64_t k, const uint16_t* a, const uint8_t* qw,
-                        const float* w_scale, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
-  W16Args args{a, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
+template <int FMT>
+hipError_t launch_fmt(int id, const W16Args& args, hipStream_t stream) {
   switch (id) {
-    case 0: return launch<256, 256, 2, 4, 3, 4>(args, stream);
-    case 1: return launch<256, 128, 4, 2, 3, 4>(args, stream);
-    case 2: return launch<128, 256, 2, 4, 4, 4>(args, stream);
-    case 3: return launch<128, 128, 2, 2, 3, 8>(args, stream);
-    case 4: return launch<64, 64, 2, 2, 3, 8>(args, stream);
+    case 0: return launch<256, 256, 2, 4, 3, 4, FMT>(args, stream);
+    case 1: return launch<256, 128, 4, 2, 3, 4, FMT>(args, stream);
+    case 2: return launch<128, 256, 2, 4, 4, 4, FMT>(args, stream);
+    case 3: return launch<128, 128, 2, 2, 3, 8, FMT>(args, stream);
+    case 4: return launch<64, 64, 2, 2, 3, 8, FMT>(args, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_w8a16(int id, int w_format, int64_t m, int64_t n, int64_t k, const uint16_t* a, const uint8_t* qw,
+                        const float* w_scale, const uint16_t* bias, uint16_t* out, hipStream_t stream) {
+  W16Args args{a, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
+  return w_format == FP8W8A8_FMT_E5M2 ? launch_fmt<FP8W8A8_FMT_E5M2>(id, args, stream)
+                                      : launch_fmt<FP8W8A8_FMT_E4M3FN>(id, args, stream);
 }
 
 }  // namespace fp8w8a8

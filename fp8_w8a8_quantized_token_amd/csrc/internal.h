@@ -59,7 +59,8 @@ int w8a16_config_count();
 const GemmConfig* w8a16_config(int id);
 int64_t w8a16_workgroups(int id, int64_t m, int64_t n);
 int w8a16_threads(int id);
-hipError_t launch_w8a16(int id, int64_t m, int64_t n, int64_t k, const uint16_t* a, const uint8_t* qw,
+// w_format: FP8W8A8_FMT_E4M3FN or FP8W8A8_FMT_E5M2 codes in qw.
+hipError_t launch_w8a16(int id, int w_format, int64_t m, int64_t n, int64_t k, const uint16_t* a, const uint8_t* qw,
                         const float* w_scale, const uint16_t* bias, uint16_t* out, hipStream_t stream);
 
 }  // namespace fp8w8a8

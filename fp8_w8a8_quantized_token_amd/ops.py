@@ -256,29 +256,37 @@ class Fp8WeightOnlyLinear:
     activation is used as it is, in bf16, and the product runs on the bf16 matrix cores.
     """
 
-    def __init__(self, weight=None, bias=None, *, w_fp8=None, w_scale=None):
+    def __init__(self, weight=None, bias=None, *, w_fp8=None, w_scale=None, fmt="e4m3fn"):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
         if weight is not None:
             if w_fp8 is not None or w_scale is not None:
                 raise ValueError("pass either a bf16 weight or (w_fp8, w_scale), not both")
+            if fmt != "e4m3fn":
+                raise ValueError("a bf16 weight is quantised per channel to e4m3fn; pass e5m2 codes as w_fp8")
             w_fp8, w_scale = quant_weights_per_channel(weight)
         if w_fp8 is None or w_scale is None:
             raise ValueError("Fp8WeightOnlyLinear needs a bf16 weight or a pre-quantised (w_fp8, w_scale)")
+        if w_fp8.dtype == torch.float8_e5m2:
+            w_fp8 = w_fp8.view(torch.uint8)
         w_fp8 = _codes(w_fp8)
         _require(w_fp8, (torch.uint8,), "w_fp8", 2)
         _require(w_scale, (torch.float32,), "w_scale", 1)
         n, k = w_fp8.shape
+        if w_scale.numel() == 1 and n > 1:  # a per-tensor scale: repeat it per channel
+            w_scale = w_scale.reshape(1).expand(n).contiguous()
         if w_scale.shape[0] != n:
-            raise ValueError("w_scale must have one entry per output channel")
+            raise ValueError("w_scale must have one entry per output channel (or a single per-tensor entry)")
         if bias is not None:
             _require(bias, (torch.bfloat16,), "bias", 1)
             if bias.shape[0] != n:
                 raise ValueError("bias must have one entry per output channel")
         self.w_fp8, self.w_scale, self.bias = w_fp8, w_scale, bias  # the plan borrows these
-        self.n, self.k = n, k
+        self.n, self.k, self.fmt = n, k, fmt
         self.device = w_fp8.device
         plan = ctypes.c_void_p()
-        check(lib().fp8_w8a16_create(self.device.index or 0, n, k, _ptr(w_fp8), _ptr(w_scale), _ptr(bias),
-                                     ctypes.byref(plan)), "fp8_w8a16_create")
+        check(lib().fp8_w8a16_create(self.device.index or 0, n, k, FORMATS[fmt], _ptr(w_fp8), _ptr(w_scale),
+                                     _ptr(bias), ctypes.byref(plan)), "fp8_w8a16_create")
         self._plan = plan
         self._lib = lib()
 
@@ -319,8 +327,10 @@ def w8a16_config_count():
     return lib().fp8_w8a16_config_count()
 
 
-def w8a16_run_config(config_id, a, w_fp8, w_scale, bias=None, out=None):
+def w8a16_run_config(config_id, a, w_fp8, w_scale, bias=None, out=None, fmt="e4m3fn"):
     """Test hook: run W8A16 configuration `config_id` directly (every configuration is held to parity)."""
+    if w_fp8.dtype == torch.float8_e5m2:
+        w_fp8 = w_fp8.view(torch.uint8)
     w_fp8 = _codes(w_fp8)
     _require(a, (torch.bfloat16,), "a", 2)
     _require(w_fp8, (torch.uint8,), "w_fp8", 2)
@@ -328,8 +338,8 @@ def w8a16_run_config(config_id, a, w_fp8, w_scale, bias=None, out=None):
     n = w_fp8.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
-    check(lib().fp8_w8a16_run_config(config_id, m, n, k, _ptr(a), _ptr(w_fp8), _ptr(w_scale), _ptr(bias),
-                                     _ptr(out), _stream(a)), "fp8_w8a16_run_config")
+    check(lib().fp8_w8a16_run_config(config_id, FORMATS[fmt], m, n, k, _ptr(a), _ptr(w_fp8), _ptr(w_scale),
+                                     _ptr(bias), _ptr(out), _stream(a)), "fp8_w8a16_run_config")
     return out
 
 

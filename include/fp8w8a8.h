@@ -282,8 +282,10 @@ int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* sc
  *
  * The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
  * (longcat-avatar-compare.pages.dev, speed overview table): the weight is stored as
- * e4m3fn codes with per-output-channel scales (fp8_quant_weights_per_channel), the
- * activation stays bf16 and is not quantised:
+ * FP8 codes with per-output-channel scales (fp8_quant_weights_per_channel; a
+ * per-tensor scale from fp8_quant_tensor is the same scale repeated n times), the
+ * activation stays bf16 and is not quantised. w_format selects the codes:
+ * FP8W8A8_FMT_E4M3FN, or FP8W8A8_FMT_E5M2 (the state-dict converter's default):
  *
  *   out[m,n] = bf16_rne( fl32( sum_k a[m,k] * dec(qW[n,k]) ) * sW[n] + bias[n] )
  *
@@ -296,7 +298,7 @@ int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* sc
  */
 typedef struct fp8_w8a16_plan fp8_w8a16_plan;
 
-int fp8_w8a16_create(int device, int64_t n, int64_t k, const void* w_fp8, const float* w_scale,
+int fp8_w8a16_create(int device, int64_t n, int64_t k, int w_format, const void* w_fp8, const float* w_scale,
                      const void* bias_bf16, fp8_w8a16_plan** out);
 
 /* m == 0 is a no-op. a_bf16 and out_bf16 are device pointers, 16-byte aligned. */
@@ -308,8 +310,8 @@ void fp8_w8a16_destroy(fp8_w8a16_plan* plan);
 int fp8_w8a16_plan_config(const fp8_w8a16_plan* plan, int64_t m, int* config_id, int* tile_m, int* tile_n,
                           int64_t* workgroups);
 int fp8_w8a16_config_count(void);
-int fp8_w8a16_run_config(int config_id, int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,
-                         const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream);
+int fp8_w8a16_run_config(int config_id, int w_format, int64_t m, int64_t n, int64_t k, const void* a_bf16,
+                         const void* w_fp8, const float* w_scale, const void* bias_bf16, void* out_bf16, void* stream);
 
 #ifdef __cplusplus
 }

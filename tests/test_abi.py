@@ -169,21 +169,23 @@ def test_act_binding_rejects_unknown_kind():
 def test_w8a16_validation(lib):
     A = ALIGNED
     plan = ctypes.c_void_p()
-    assert lib.fp8_w8a16_create(0, 16, 16, A, A, None, None) == _lib.ERR_INVALID_ARG
-    assert lib.fp8_w8a16_create(0, 16, 16, None, A, None, ctypes.byref(plan)) == _lib.ERR_INVALID_ARG
+    assert lib.fp8_w8a16_create(0, 16, 16, 0, A, A, None, None) == _lib.ERR_INVALID_ARG
+    assert lib.fp8_w8a16_create(0, 16, 16, 0, None, A, None, ctypes.byref(plan)) == _lib.ERR_INVALID_ARG
+    assert lib.fp8_w8a16_create(0, 16, 16, 7, A, A, None, ctypes.byref(plan)) == _lib.ERR_INVALID_ARG
     for n, k in ((0, 16), (16, 0), (24, 32), (16, 40)):
-        assert lib.fp8_w8a16_create(0, n, k, A, A, None, ctypes.byref(plan)) == _lib.ERR_BAD_SHAPE, (n, k)
-    assert lib.fp8_w8a16_create(0, 16, 16, MIS16, A, None, ctypes.byref(plan)) == _lib.ERR_MISALIGNED
+        assert lib.fp8_w8a16_create(0, n, k, 1, A, A, None, ctypes.byref(plan)) == _lib.ERR_BAD_SHAPE, (n, k)
+    assert lib.fp8_w8a16_create(0, 16, 16, 0, MIS16, A, None, ctypes.byref(plan)) == _lib.ERR_MISALIGNED
     assert lib.fp8_w8a16_run(None, 4, A, A, None) == _lib.ERR_INVALID_ARG
     lib.fp8_w8a16_destroy(None)
     n = lib.fp8_w8a16_config_count()
     assert n >= 1
-    args = (4, 16, 16, A, A, A, None, A, None)
+    args = (0, 4, 16, 16, A, A, A, None, A, None)
     assert lib.fp8_w8a16_run_config(-1, *args) == _lib.ERR_INVALID_ARG
     assert lib.fp8_w8a16_run_config(n, *args) == _lib.ERR_INVALID_ARG
-    assert lib.fp8_w8a16_run_config(0, 4, 16, 24, A, A, A, None, A, None) == _lib.ERR_BAD_SHAPE
-    assert lib.fp8_w8a16_run_config(0, 4, 16, 16, MIS16, A, A, None, A, None) == _lib.ERR_MISALIGNED
-    assert lib.fp8_w8a16_run_config(0, 0, 16, 16, A, A, A, None, A, None) == _lib.OK
+    assert lib.fp8_w8a16_run_config(0, 3, 4, 16, 16, A, A, A, None, A, None) == _lib.ERR_INVALID_ARG
+    assert lib.fp8_w8a16_run_config(0, 0, 4, 16, 24, A, A, A, None, A, None) == _lib.ERR_BAD_SHAPE
+    assert lib.fp8_w8a16_run_config(0, 1, 4, 16, 16, MIS16, A, A, None, A, None) == _lib.ERR_MISALIGNED
+    assert lib.fp8_w8a16_run_config(0, 0, 0, 16, 16, A, A, A, None, A, None) == _lib.OK
 
 
 def test_tensor_quant_validation(lib):

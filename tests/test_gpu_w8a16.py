@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import fp8_w8a8_quantized_token_amd as fp8
-from oracle import e4m3, quant as oq, w8a16 as ow
+from oracle import e4m3, e5m2, quant as oq, tensor_quant as otq, w8a16 as ow
 from tests._helpers import assert_linear_close, require_gpu, sample_rows
 from workloads import bf16_bits, make_case, make_config
 
@@ -63,21 +63,30 @@ def test_every_config_on_ragged_tails(config, m, n, k):
 
 @pytest.mark.parametrize("config", range(N_CONFIGS))
 def test_every_e4m3_code_through_the_conversion(config):
+    _every_code(config, "e4m3fn", np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8))
+
+
+@pytest.mark.parametrize("config", range(N_CONFIGS))
+def test_every_e5m2_code_through_the_conversion(config):
+    _every_code(config, "e5m2", np.array([c for c in range(256) if (c & 0x7F) < 0x7C], np.uint8))
+
+
+def _every_code(config, fmt, codes):
     # one-hot activation rows pick single weight codes: out[t, n] = dec(qw[n, t]) exactly
     dev = require_gpu()
-    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)  # 254 finite codes
+    dec = e4m3.decode if fmt == "e4m3fn" else e5m2.decode
     k = 256
     n = 64
-    rng = np.random.default_rng(config)
-    qw = np.empty((n, k), np.uint8)
+    rng = np.random.default_rng(config + 17 * len(codes))
+    qw = np.zeros((n, k), np.uint8)
     for r in range(n):
-        qw[r, :254] = rng.permutation(codes)
-        qw[r, 254:] = 0
-    a = torch.eye(k, dtype=torch.bfloat16)[:200]  # rows 0..199
+        qw[r, :len(codes)] = rng.permutation(codes)
+    a = torch.eye(k, dtype=torch.bfloat16)[:len(codes)]
     sw = np.ones(n, np.float32)
-    out = fp8.w8a16_run_config(config, a.to(dev), torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev))
+    out = fp8.w8a16_run_config(config, a.to(dev), torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev),
+                               fmt=fmt)
     got = out.float().cpu().numpy()
-    exp = e4m3.decode(qw[:, :200]).T  # e4m3 values are exact in bf16
+    exp = dec(qw[:, :len(codes)]).T  # every finite code's value is exact in bf16
     assert np.array_equal(got, exp.astype(np.float32))
 
 
@@ -104,6 +113,20 @@ def test_selector_and_3d_input():
     assert out.shape == (4, 24, 400)
     ref, _, _ = _ref(case)
     assert_linear_close(out.reshape(96, 400), ref, "w8a16 3-d input")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
+def test_per_tensor_weights_from_the_state_dict_converter(fmt):
+    # the converter's output (codes + one scale) runs through the weight-only linear
+    dev = require_gpu()
+    case = make_case(130, 272, 528, seed=12, kind="normal")
+    q, s = fp8.quant_tensor(case.w.to(dev), fmt)
+    lin = fp8.Fp8WeightOnlyLinear(w_fp8=q, w_scale=s, bias=case.bias.to(dev), fmt=fmt)
+    out = lin(case.a.to(dev))
+    eq, es = otq.quant_tensor(bf16_bits(case.w), fmt)
+    assert np.array_equal(q.cpu().numpy(), eq)
+    ref = ow.w8a16_ref(bf16_bits(case.a), eq, np.full(272, es, np.float32), bf16_bits(case.bias), fmt=fmt)
+    assert_linear_close(out, ref, f"w8a16 per-tensor {fmt}")
 
 
 @pytest.mark.slow
