@@ -181,6 +181,65 @@ def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
             "config": {"id": cid, "tile_m": tm, "tile_n": tn, "workgroups": wg}}
 
 
+def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
+    """The FFN-up step as one launch (fp8_quant_gemm) against the same step as two
+    launches (fp8_quant_rows, then GEMM configuration 0), same inputs and loop shape:
+    events only at the ends of `steps` back-to-back steps."""
+    from workloads.synth import activation, bias as gen_bias, weight
+    from fp8_w8a8_quantized_token_amd import _lib
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    ws_bytes = lib.fp8_quant_gemm_workspace_bytes(M, K)
+    codes_bytes = (M * K + 255) // 256 * 256
+    sets = []
+    for i in range(nsets):
+        a = activation(0, 2, 70 + i, M, K, "normal").to(dev)
+        qw, sw = fp8.quant_weights_per_channel(weight(0, 2, 170 + i, N, K).to(dev))
+        b = gen_bias(0, 2, 270 + i, N).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        sets.append((a, qw, sw, b, out, ws))
+    torch.cuda.synchronize()
+
+    def one(i):
+        a, qw, sw, b, out, ws = sets[i % nsets]
+        st = lib.fp8_quant_gemm(M, N, K, P(a), P(qw), P(sw), P(b), P(out), P(ws), ws_bytes, sptr)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_quant_gemm")
+
+    def two(i):
+        a, qw, sw, b, out, ws = sets[i % nsets]
+        scales = ctypes.c_void_p(ws.data_ptr() + codes_bytes)
+        st = lib.fp8_quant_rows(P(a), M, K, P(ws), scales, sptr)
+        st = st or lib.fp8_gemm_run_config(0, M, N, K, P(ws), scales, P(qw), P(sw), P(b), P(out), sptr)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows / fp8_gemm_run_config")
+
+    res = {}
+    for name, run in (("two_launch", two), ("single_launch", one), ("two_launch_again", two),
+                      ("single_launch_again", one)):
+        for i in range(5):
+            run(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps * 1e3
+    del sets
+    torch.cuda.empty_cache()
+    two_us = min(res["two_launch"], res["two_launch_again"])
+    one_us = min(res["single_launch"], res["single_launch_again"])
+    flop = 2.0 * M * N * K
+    return {"kernel": "gemm_fp8_kernel (single-launch form)", "M": M, "N": N, "K": K, "steps": steps,
+            "single_launch_us_per_step": round(one_us, 3), "two_launch_us_per_step": round(two_us, 3),
+            "single_launch_tflops": round(flop / (one_us * 1e-6) / 1e12, 2),
+            "two_launch_tflops": round(flop / (two_us * 1e-6) / 1e12, 2),
+            "speedup": round(two_us / one_us, 4)}
+
+
 def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
     """Per-tensor quantisation (both formats): two launches, HBM-resident rotating inputs."""
     from fp8_w8a8_quantized_token_amd import _lib
@@ -269,6 +328,7 @@ def main():
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
     ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
     ap.add_argument("--no-tensor-quant", action="store_true", help="skip the per-tensor quantisation timing")
+    ap.add_argument("--no-quant-gemm", action="store_true", help="skip the single-launch quant + GEMM timing")
     ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
                     help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -417,6 +477,8 @@ def main():
         result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if not args.no_tensor_quant:
         result["tensor_quant"] = tensor_quant_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 50)))
+    if not args.no_quant_gemm:
+        result["quant_gemm"] = quant_gemm_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
     if args.copy_calibration:
         copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}

@@ -21,6 +21,7 @@ from .ops import (  # noqa: F401
     gemm_config_count,
     gemm_run_config,
     linear,
+    quant_gemm,
     quant_rows,
     quant_weights_per_channel,
     w8a16_config_count,
@@ -44,6 +45,7 @@ __all__ = [
     "quant_weights_per_channel",
     "gemm_config_count",
     "gemm_run_config",
+    "quant_gemm",
     "lib",
     "LIB_PATH",
     "A_BF16",

@@ -69,6 +69,9 @@ SIGNATURES = {
                                             _c_p, _c_p, _c_p]),
     "fp8_gemm_run_config": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                            _c_p, _c_p]),
+    "fp8_quant_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "fp8_quant_gemm": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t,
+                                      _c_p]),
 }
 
 

@@ -13,6 +13,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "internal.h"
 
@@ -175,6 +177,18 @@ int bucket_config(const Family& f, const int64_t* max_m, const int* config, int6
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Launch epochs of the single-launch quant + GEMM: unique within the process (a
+// counter) and unlikely to repeat another process's (a random 64-bit start), so a
+// workspace's flags from any earlier launch never match the current one.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    return ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^
+           (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed);
+}
 
 }  // namespace
 
@@ -402,6 +416,34 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
   hipError_t e = launch_gemm(config_id, m, n, k, static_cast<const uint8_t*>(qa), a_scale,
                              static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
                              static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+size_t fp8_quant_gemm_workspace_bytes(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0) return 0;
+  return align256((size_t)m * (size_t)k) + align256((size_t)m * sizeof(float)) +
+         (size_t)kQuantGemmMaxWorkgroups * sizeof(unsigned long long);
+}
+
+int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8, const float* w_scale,
+                   const void* bias_bf16, void* out_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a_bf16 || !out_bf16 || !workspace) return FP8W8A8_ERR_INVALID_ARG;
+  int st = check_weight_args(n, k, w_fp8, w_scale, bias_bf16);
+  if (st != FP8W8A8_OK) return st;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(a_bf16, 16) || !aligned(out_bf16, 16) || !aligned(workspace, 256)) return FP8W8A8_ERR_MISALIGNED;
+  if (workspace_bytes < fp8_quant_gemm_workspace_bytes(m, k)) return FP8W8A8_ERR_WORKSPACE_TOO_SMALL;
+  if (m == 0) return FP8W8A8_OK;
+  int cus = 0;
+  st = current_device_ok(&cus);
+  if (st != FP8W8A8_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* ws_scale = reinterpret_cast<float*>(ws + align256((size_t)m * (size_t)k));
+  auto* flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<uint8_t*>(ws_scale) +
+                                                      align256((size_t)m * sizeof(float)));
+  hipError_t e = launch_quant_gemm(m, n, k, static_cast<const uint16_t*>(a_bf16), ws, ws_scale, flags, next_epoch(),
+                                   static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
+                                   static_cast<uint16_t*>(out_bf16), cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 

@@ -34,8 +34,20 @@
 //     rounding to bf16. The bf16 tile is then staged through LDS as well, so the
 //     output leaves in whole 128-byte lines (16 bytes per lane) instead of scattered
 //     8-byte pieces.
+//   * A single-launch form (FUSED, 256 x 256 tiles) takes the bf16 activation instead
+//     of its codes: the option of one kernel for the run-time quantisation and the
+//     GEMM that section 3.2 of the page points towards (quantisation and its memory
+//     traffic as a cost of the FP8 path). Per-token scales need a token's whole row
+//     before its first code and a tile needs all k of its tokens, so the first wave of
+//     workgroups quantises the tokens in shares (the per-token quantiser's arithmetic,
+//     bit for bit) and flags each share; every workgroup waits for all flags, then runs
+//     its tile as above. The weight half of the first stages is requested before the
+//     quantisation so it lands meanwhile.
+#include <algorithm>
+
 #include "internal.h"
 #include "gemm_common.h"
+#include "quant_row.h"
 
 namespace fp8w8a8 {
 namespace {
@@ -49,14 +61,126 @@ struct GemmArgs {
   uint16_t* out;
   int m, n, k;
   int tiles_m, tiles_n;
+  // single-launch form only: the bf16 activation, its per-token shares and their flags
+  const uint16_t* a_bf16;
+  uint8_t* qa_out;     // == qa
+  float* a_scale_out;  // == a_scale
+  unsigned long long* flags;
+  unsigned long long epoch;
+  int shares, rows_per_share;
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
+constexpr int kScDevice = 16;  // cache-policy bit sc1: device-scope coherent access
+constexpr uint64_t kStealAfterTicks = 10000;  // 100 us of the 100 MHz real-time clock
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Per-token results of the single-launch form are stored with device scope (sc1):
+// written through the XCD's L2 to the device coherence point, and counted complete
+// (vmcnt) only once visible there. A workgroup that has waited for its own stores can
+// publish its flag without an L2 write-back (a release fence would write back the
+// whole L2; issued by every workgroup at once that costs tens of microseconds).
+struct DeviceScopeStore {
+  __device__ __forceinline__ void codes(uint8_t* qr, int c, int nchunks, const uint4& v) const {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(qr, 0, nchunks * 16, kBufferConfig);
+    const v4u data = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(data, r, c * 16, 0, kScDevice);
+  }
+  __device__ __forceinline__ void scale(float* srow, float s) const {
+    __hip_atomic_store(reinterpret_cast<unsigned*>(srow), __float_as_uint(s), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+// Quantise the tokens of share `sh` (rows [sh * R, (sh + 1) * R) clipped to m), one
+// wavefront per token, two tokens in flight per wavefront, then publish the share.
+template <int NC, int WAVES>
+__device__ __forceinline__ void quant_share_rows(const GemmArgs& args, int r_begin, int r_end, int wave, int lane) {
+  const int K = args.k;
+  const int nchunks = K >> 4;
+  if constexpr (NC > 0) {
+    for (int r = r_begin + wave; r < r_end; r += 2 * WAVES) {
+      const int r2 = r + WAVES;
+      uint4 va[NC], vb[NC], wa[NC], wb[NC];
+      qrow::load_row<NC>(args.a_bf16 + (int64_t)r * K, nchunks, lane, va, vb);
+      if (r2 < r_end) qrow::load_row<NC>(args.a_bf16 + (int64_t)r2 * K, nchunks, lane, wa, wb);
+      qrow::quant_row<NC>(va, vb, nchunks, lane, args.qa_out + (int64_t)r * K, args.a_scale_out + r,
+                          DeviceScopeStore{});
+      if (r2 < r_end)
+        qrow::quant_row<NC>(wa, wb, nchunks, lane, args.qa_out + (int64_t)r2 * K, args.a_scale_out + r2,
+                            DeviceScopeStore{});
+    }
+  } else {
+    for (int r = r_begin + wave; r < r_end; r += WAVES)
+      qrow::quant_row_loop(args.a_bf16 + (int64_t)r * K, nchunks, lane, args.qa_out + (int64_t)r * K,
+                           args.a_scale_out + r, qrow::NoMap{}, DeviceScopeStore{});
+  }
+}
+
+template <int WAVES>
+__device__ __forceinline__ void quant_share(const GemmArgs& args, int sh, int wave, int lane) {
+  const int r_begin = min(sh * args.rows_per_share, args.m);
+  const int r_end = min(r_begin + args.rows_per_share, args.m);
+  const int nc = ((args.k >> 4) + 63) / 64;
+  if (nc <= 1) quant_share_rows<1, WAVES>(args, r_begin, r_end, wave, lane);
+  else if (nc <= 2) quant_share_rows<2, WAVES>(args, r_begin, r_end, wave, lane);
+  else if (nc <= 4) quant_share_rows<4, WAVES>(args, r_begin, r_end, wave, lane);
+  else if (nc <= 8) quant_share_rows<8, WAVES>(args, r_begin, r_end, wave, lane);
+  else quant_share_rows<0, WAVES>(args, r_begin, r_end, wave, lane);
+  wait_vm_lgkm0<0>();  // this wavefront's device-scope stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(args.flags + sh, args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every share carries this launch's epoch. Wavefront 0 polls; a share still
+// unpublished after kStealAfterTicks is quantised here as well (identical bytes, so a
+// duplicate writer is harmless), so the wait ends even if the share's own workgroup is
+// not resident. Ends with an agent-scope acquire so the GEMM reads see every share.
+template <int WAVES>
+__device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int lane, int* slot) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    if (wave == 0) {
+      int missing = -1;
+      while (true) {
+        int first = -1;
+        for (int j0 = 0; j0 < args.shares; j0 += 64) {
+          const int j = j0 + lane;
+          const bool miss =
+              j < args.shares &&
+              __hip_atomic_load(args.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != args.epoch;
+          const unsigned long long b = __ballot(miss);
+          if (b != 0 && first < 0) first = j0 + __builtin_ctzll(b);
+        }
+        if (first < 0) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kStealAfterTicks) {
+          missing = first;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) *slot = missing;
+    }
+    __syncthreads();
+    const int sh = __builtin_amdgcn_readfirstlane(*slot);
+    __syncthreads();  // every wave has read the slot before wavefront 0 may rewrite it
+    if (sh < 0) break;
+    quant_share<WAVES>(args, sh, wave, lane);
+  }
+  if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // L1 / L2 invalidate
+  __syncthreads();
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED>
 struct KernelTag {};
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M>
+// FUSED: the single-launch form. The activation codes and scales do not exist yet at
+// launch: the first `shares` workgroups quantise the bf16 activation into them
+// (quant_share), every workgroup waits for all shares (await_shares), and the weight
+// half of the first stages is requested before all that so it lands meanwhile.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
-  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M>;
+  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED>;
   static_assert(BK == 64 || BK == 128, "stage depth in k bytes");
   constexpr int H = BK / 64;         // 32x32x64 MFMA k-steps per stage
   constexpr int CPR = BK / 16;       // 16-byte chunks per tile row
@@ -77,6 +201,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert((BM / RPF) % kWaves == 0, "activation fills split evenly across waves");
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
   static_assert((BM + 2 * BN) * 4 <= kStageBytes, "epilogue staging fits in one stage");
+  static_assert(!FUSED || STAGES == 2, "the single-launch prologue's fill order assumes two stages");
+  constexpr int FA = (BM / RPF) / kWaves;  // activation fills per wave per stage
 
   auto buf = [](int s) -> uint8_t* {
     switch (s) {
@@ -107,7 +233,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   // latency hides behind the k loop.
   const int tid = threadIdx.x;
   float pre_sa = 0.0f, pre_sw = 0.0f, pre_b = 0.0f;
-  if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
+  if constexpr (!FUSED)
+    if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
   if (tid < BN && tid < rows_w) {
     pre_sw = args.w_scale[n0 + tid];
     if (args.bias) pre_b = __uint_as_float((uint32_t)args.bias[n0 + tid] << 16);
@@ -124,17 +251,19 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   const uint32_t foff0 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0;
   const uint32_t foff1 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1;
 
-  auto issue = [&](uint8_t* base, int k0) {
+  // part: 0 = the whole stage, 1 = activation rows only, 2 = weight rows only
+  auto issue = [&](uint8_t* base, int k0, int part = 0) {
     const bool kvalid0 = k0 + 16 * fchunk0 < K;
     const bool kvalid1 = k0 + 16 * fchunk1 < K;
 #pragma unroll
     for (int j = 0; j < F; ++j) {
+      if ((part == 1 && j >= FA) || (part == 2 && j < FA)) continue;
       const int g = wave + j * kWaves;
       const bool odd = ((g * RPF) & 15) != 0;
       const bool kvalid = odd ? kvalid1 : kvalid0;
       const uint32_t foff = odd ? foff1 : foff0;
       const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
-      if (j < (BM / RPF) / kWaves) {
+      if (j < FA) {
         const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_a, dst, vo);
       } else {
@@ -202,11 +331,28 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   // finished reading stage t, whose buffer is then refilled with stage t + STAGES.
   const int nst = (K + BK - 1) / BK;
   const int nsub = nst * H;
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nst) issue(buf(s), s * BK);
   Frags f0, f1;
-  wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+  if constexpr (FUSED) {
+    // weight fills first; the activation codes are produced in this launch
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue(buf(s), s * BK, 2);
+    __shared__ int steal_slot;
+    if (blockIdx.x < (unsigned)args.shares) quant_share<kWaves>(args, blockIdx.x, wave, lane);
+    await_shares<kWaves>(args, wave, lane, &steal_slot);
+    if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue(buf(s), s * BK, 1);
+    // stage 0 is complete once at most the younger stage's activation fills remain
+    if (nst > 1) wait_vm_lgkm0<FA>();
+    else wait_vm_lgkm0<0>();
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue(buf(s), s * BK);
+    wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+  }
   block_barrier();
   read_frags(buf(0), 0, f0);
 
@@ -312,13 +458,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   }
 }
 
-template <int BM, int BN, int WM, int WN, int S, int BK, int GM>
+template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
   const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -361,6 +507,22 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_quant_gemm(int64_t m, int64_t n, int64_t k, const uint16_t* a_bf16, uint8_t* qa_ws, float* sa_ws,
+                             unsigned long long* flags, unsigned long long epoch, const uint8_t* qw,
+                             const float* w_scale, const uint16_t* bias, uint16_t* out, int cus, hipStream_t stream) {
+  GemmArgs a{qa_ws, sa_ws, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
+  a.a_bf16 = a_bf16;
+  a.qa_out = qa_ws;
+  a.a_scale_out = sa_ws;
+  a.flags = flags;
+  a.epoch = epoch;
+  // one share per workgroup of the first wave (one 256 x 256 workgroup per CU)
+  const int64_t tiles = gemm_workgroups(0, m, n);
+  a.shares = (int)std::min<int64_t>({tiles, (int64_t)cus, (int64_t)kQuantGemmMaxWorkgroups});
+  a.rows_per_share = (int)((m + a.shares - 1) / a.shares);
+  return launch<256, 256, 2, 4, 2, 128, 4, true>(a, stream);
 }
 
 }  // namespace fp8w8a8

@@ -54,6 +54,16 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
                        const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
                        hipStream_t stream);
 
+// Per-token quantisation and the FP8 GEMM (configuration 0) in one launch. qa_ws [m, k]
+// and sa_ws [m] receive the codes and scales (as launch_quant_rows writes them); flags
+// holds kQuantGemmMaxWorkgroups 64-bit words of any prior content; epoch must differ
+// from every epoch used before with the same flags. cus: the device's compute units
+// (one share of the tokens per workgroup of the first wave).
+constexpr int kQuantGemmMaxWorkgroups = 1024;
+hipError_t launch_quant_gemm(int64_t m, int64_t n, int64_t k, const uint16_t* a_bf16, uint8_t* qa_ws, float* sa_ws,
+                             unsigned long long* flags, unsigned long long epoch, const uint8_t* qw,
+                             const float* w_scale, const uint16_t* bias, uint16_t* out, int cus, hipStream_t stream);
+
 // The FP8 weight-only (W8A16) GEMM: out[m, n] = bf16(sum_k a[m, k] dec(qw[n, k]) * w_scale[n] + bias[n]).
 int w8a16_config_count();
 const GemmConfig* w8a16_config(int id);

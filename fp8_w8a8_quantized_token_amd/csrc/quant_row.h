@@ -99,23 +99,32 @@ __device__ __forceinline__ void load_row(const uint16_t* xr, int nchunks, int la
   }
 }
 
+// How a row's results reach memory: plain stores (the default), or a policy with the
+// same two members (the single-launch quantise + GEMM kernel writes through to the
+// device coherence point). `qr` is the row's code pointer (uniform across the
+// wavefront), `c` a 16-code chunk index.
+struct PlainStore {
+  __device__ __forceinline__ void codes(uint8_t* qr, int c, int, const uint4& v) const {
+    *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = v;
+  }
+  __device__ __forceinline__ void scale(float* srow, float s) const { *srow = s; }
+};
+
 // Scale and codes of a register-resident row (every lane of the wavefront calls it).
-template <int NC>
+template <int NC, class Store = PlainStore>
 __device__ __forceinline__ void quant_row(const uint4 (&va)[NC], const uint4 (&vb)[NC], int nchunks, int lane,
-                                          uint8_t* qr, float* srow) {
+                                          uint8_t* qr, float* srow, const Store& st = Store{}) {
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NC; ++j) amax = absmax16(amax, va[j], vb[j]);
   amax = wave_max(amax);
   const float s = amax / 448.0f;
-  if (lane == 0) *srow = s;
+  if (lane == 0) st.scale(srow, s);
 
 #define FP8W8A8_QUANT_STORE(MODE, R)                                                     \
   _Pragma("unroll") for (int j = 0; j < NC; ++j) {                                       \
     const int c = j * 64 + lane;                                                         \
-    if (c < nchunks)                                                                     \
-      *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) =                     \
-          quant16<MODE>(va[j], vb[j], s, R);                                             \
+    if (c < nchunks) st.codes(qr, c, nchunks, quant16<MODE>(va[j], vb[j], s, R));        \
   }
   if (amax >= kTinyAmax) {
     const float r = 1.0f / s;
@@ -135,9 +144,9 @@ struct NoMap {
 
 // Rows longer than the register-resident variants: the row is read twice (the
 // second read is served by L2); `map` is applied to every chunk on both passes.
-template <class Map>
+template <class Map, class Store = PlainStore>
 __device__ __forceinline__ void quant_row_loop(const uint16_t* xr, int nchunks, int lane, uint8_t* qr,
-                                               float* srow, const Map& map) {
+                                               float* srow, const Map& map, const Store& st = Store{}) {
   float amax = 0.0f;
   for (int c = lane; c < nchunks; c += 64) {
     const uint4* p = reinterpret_cast<const uint4*>(xr + static_cast<int64_t>(c) * 16);
@@ -148,7 +157,7 @@ __device__ __forceinline__ void quant_row_loop(const uint16_t* xr, int nchunks, 
   }
   amax = wave_max(amax);
   const float s = amax / 448.0f;
-  if (lane == 0) *srow = s;
+  if (lane == 0) st.scale(srow, s);
   const float r = 1.0f / s;
   for (int c = lane; c < nchunks; c += 64) {
     const uint4* p = reinterpret_cast<const uint4*>(xr + static_cast<int64_t>(c) * 16);
@@ -162,7 +171,7 @@ __device__ __forceinline__ void quant_row_loop(const uint16_t* xr, int nchunks, 
       o = quant16<Mode::kZero>(a, b, s, r);
     else
       o = quant16<Mode::kExact>(a, b, s, r);
-    *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = o;
+    st.codes(qr, c, nchunks, o);
   }
 }
 

@@ -374,5 +374,38 @@ def gemm_run_config(config_id, qa, a_scale, w_fp8, w_scale, bias=None, out=None)
     return out
 
 
+def quant_gemm(a, w_fp8, w_scale, bias=None, out=None, workspace=None):
+    """Per-token quantisation and the FP8 GEMM in one launch.
+
+    Returns (out [m, n] bf16, codes [m, k] uint8, scales [m] fp32); codes and scales
+    are views of the workspace that the launch wrote them to.
+    """
+    a2 = a.reshape(-1, a.shape[-1]) if a.dim() != 2 else a
+    _require(a2, (torch.bfloat16,), "a", 2)
+    w_fp8 = _codes(w_fp8)
+    _require(w_fp8, (torch.uint8,), "w_fp8", 2)
+    _require(w_scale, (torch.float32,), "w_scale", 1)
+    m, k = a2.shape
+    n = w_fp8.shape[0]
+    if w_fp8.shape[1] != k or w_scale.shape[0] != n:
+        raise ValueError("operand shapes do not agree")
+    if bias is not None:
+        _require(bias, (torch.bfloat16,), "bias", 1)
+        if bias.shape[0] != n:
+            raise ValueError("bias must have n entries")
+    ws_bytes = lib().fp8_quant_gemm_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=a2.device)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a2.device)
+    check(lib().fp8_quant_gemm(m, n, k, _ptr(a2), _ptr(w_fp8), _ptr(w_scale), _ptr(bias), _ptr(out),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(a2)),
+          "fp8_quant_gemm")
+    codes_bytes = (m * k + 255) // 256 * 256
+    codes = workspace[: m * k].view(m, k)
+    scales = workspace[codes_bytes: codes_bytes + 4 * m].view(torch.float32)
+    return out, codes, scales
+
+
 __all__ = ["quant_rows", "quant_weights_per_channel", "Fp8Linear", "linear", "gemm_config_count",
-           "gemm_run_config", "A_BF16", "A_E4M3", "_lib"]
+           "gemm_run_config", "quant_gemm", "A_BF16", "A_E4M3", "_lib"]

@@ -245,6 +245,36 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
                         const float* a_scale, const void* w_fp8, const float* w_scale,
                         const void* bias_bf16, void* out_bf16, void* stream);
 
+/* ---- single-launch quantisation + GEMM -------------------------------------------
+ *
+ * The retrospective (section 3.2) counts run-time activation quantisation and its
+ * extra memory traffic among the costs of the FP8 path. fp8_quant_gemm performs the
+ * per-token quantisation (bit-identical to fp8_quant_rows) and the GEMM with its
+ * epilogue (bit-identical to fp8_gemm_run_config's configuration 0, 256 x 256 tiles)
+ * in ONE kernel launch: the first wave of workgroups quantises the tokens in shares
+ * into the workspace and publishes a flag per share; every workgroup waits until all
+ * shares are published (quantising itself any share whose owner has not published
+ * within 100 us, so the wait ends even when not all workgroups are resident), then
+ * runs its output tile on the codes. Same result as fp8_quant_rows followed by the
+ * GEMM; on MI355X it is no faster than those two launches (see the bench's
+ * quant_gemm record), so fp8_linear_run keeps the two launches.
+ *
+ *   m, n, k    as fp8_linear_create / fp8_linear_run (0 <= m < FP8W8A8_MAX_ROWS)
+ *   a_bf16     device, bf16 [m, k], 16-byte aligned
+ *   w_fp8, w_scale, bias_bf16   as fp8_linear_create
+ *   out_bf16   device, bf16 [m, n], 16-byte aligned, written
+ *   workspace  device, 256-byte aligned, at least fp8_quant_gemm_workspace_bytes(m, k):
+ *              the codes [m, k] (rounded up to 256 bytes), then the scales [m] (likewise),
+ *              then the launch flags. After the call the codes and scales hold the
+ *              quantised activation. Prior contents do not matter (no clearing needed);
+ *              two calls that overlap in time must not share a workspace.
+ *   stream     hipStream_t or NULL; one launch, no synchronisation
+ */
+size_t fp8_quant_gemm_workspace_bytes(int64_t m, int64_t k);
+int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,
+                   const float* w_scale, const void* bias_bf16, void* out_bf16, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* ---- per-tensor FP8 quantisation (state-dict conversion) -------------------------
  *
  * The QuantizeFP8Format page (runcomfy.com, "Quantize Model to FP8 Format")

@@ -123,6 +123,28 @@ def test_run_and_helpers_validation(lib):
     assert lib.fp8_linear(A, _lib.A_BF16, None, 4, 24, 16, A, A, None, A, A, 1 << 20, None) == _lib.ERR_BAD_SHAPE
 
 
+def test_quant_gemm_validation(lib):
+    A = ALIGNED
+    need = lib.fp8_quant_gemm_workspace_bytes(300, 400)
+    # codes and scales each rounded up to 256 bytes, then 1024 launch flags of 8 bytes
+    assert need == 120064 + 1280 + 8192
+    assert lib.fp8_quant_gemm_workspace_bytes(0, 400) == 0
+    ok = (300, 272, 400, A, A, A, A, A, A, need, None)
+    bad = lambda **kw: lib.fp8_quant_gemm(*[kw.get(f, v) for f, v in zip(
+        ("m", "n", "k", "a", "w", "ws", "b", "out", "work", "bytes", "stream"), ok)])
+    assert bad(a=None) == _lib.ERR_INVALID_ARG
+    assert bad(out=None) == _lib.ERR_INVALID_ARG
+    assert bad(work=None) == _lib.ERR_INVALID_ARG
+    assert bad(w=None) == _lib.ERR_INVALID_ARG
+    assert bad(k=24) == _lib.ERR_BAD_SHAPE
+    assert bad(n=8) == _lib.ERR_BAD_SHAPE
+    assert bad(m=-1) == _lib.ERR_BAD_SHAPE
+    assert bad(a=MIS16) == _lib.ERR_MISALIGNED
+    assert bad(work=A + 128) == _lib.ERR_MISALIGNED
+    assert bad(bytes=need - 1) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert bad(m=0, bytes=0) == _lib.OK  # m == 0 is a no-op
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     from fp8_w8a8_quantized_token_amd import quant_rows
