@@ -3,7 +3,7 @@
 //   out[m, n] = bf16_rne( acc[m, n] * a_scale[m] * w_scale[n] + bias[n] ),
 //   acc[m, n] = sum_k dec(qa[m, k]) * dec(qw[n, k])   (fp32 accumulation on the MFMA units)
 //
-// This is the "FP8 GEMM" and "scale / bias / output dtype" part of the chain in the
+// This is the FP8 GEMM step and the scale / bias / output-type step of the chain in the
 // HunyuanVideo1.5 BF16->FP8 retrospective (aigcage.com, section 3.1). Both operands
 // are k-contiguous: the activation codes [m, k] and the weight in nn.Linear's [n, k]
 // layout (the page's column-major B, never transposed). Section 3.2 of the page finds

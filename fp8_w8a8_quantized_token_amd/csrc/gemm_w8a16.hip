@@ -3,7 +3,7 @@
 //   out[m, n] = bf16_rne( acc[m, n] * w_scale[n] + bias[n] ),
 //   acc[m, n] = sum_k a[m, k] * dec(qw[n, k])   (fp32 accumulation on the MFMA units)
 //
-// The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
+// The FP8 weight-only pipeline of the LongCat avatar comparison page
 // (longcat-avatar-compare.pages.dev, speed overview table) keeps the weights in FP8
 // with scales and the activations in 16-bit; the weight scale is per output channel
 // as in the HunyuanVideo1.5 retrospective (aigcage.com, section 2), so it is constant

@@ -1,8 +1,8 @@
 // Per-tensor FP8 quantisation (e4m3fn or e5m2) and fp32 dequantisation for gfx950.
 //
 // The state-dict converter of the QuantizeFP8Format page (runcomfy.com, "Quantize
-// Model to FP8 Format") turns each tensor into float8_e4m3fn or float8_e5m2 with "a
-// simple scaling technique"; the Stable Diffusion 3.5 FP8 page (dn008.com.cn, section
+// Model to FP8 Format") turns each tensor into float8_e4m3fn or float8_e5m2 by
+// scaling it (no formula given); the Stable Diffusion 3.5 FP8 page (dn008.com.cn, section
 // on FP8, steps 1-4) spells the steps out: the largest magnitude, a scale, x / scale
 // rounded to the 8-bit format, and x_q * scale back in fp32. One scale per tensor:
 //

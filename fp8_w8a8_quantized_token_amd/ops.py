@@ -250,7 +250,7 @@ class Fp8Linear:
 class Fp8WeightOnlyLinear:
     """An FP8 weight-only (W8A16) linear: e4m3fn weight with per-channel scales, bf16 activation.
 
-    The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
+    The FP8 weight-only pipeline of the LongCat avatar comparison page
     (longcat-avatar-compare.pages.dev, speed overview): the weight is quantised per
     output channel once at construction (or passed in as (w_fp8, w_scale)); the
     activation is used as it is, in bf16, and the product runs on the bf16 matrix cores.

@@ -38,7 +38,7 @@
  * retrospective moves such decisions out of the forward call). Device faults
  * are asynchronous and surface at the caller's next synchronisation, as usual
  * in HIP. Rows m == 0 are a no-op returning FP8W8A8_OK; an empty weight
- * (n == 0 or k == 0) is FP8W8A8_ERR_BAD_SHAPE, like the "Invalid input." error
+ * (n == 0 or k == 0) is FP8W8A8_ERR_BAD_SHAPE, like the empty-input error
  * that the ComfyUI FP8 quantiser page (runcomfy.com, "Quantize Model to FP8
  * Format", common errors) gives for an empty model.
  */
@@ -278,8 +278,8 @@ int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const vo
 /* ---- per-tensor FP8 quantisation (state-dict conversion) -------------------------
  *
  * The QuantizeFP8Format page (runcomfy.com, "Quantize Model to FP8 Format")
- * converts each tensor to float8_e4m3fn or float8_e5m2 with "a simple scaling
- * technique"; the Stable Diffusion 3.5 FP8 page (dn008.com.cn, section on FP8,
+ * converts each tensor to float8_e4m3fn or float8_e5m2 by scaling it (no formula
+ * given); the Stable Diffusion 3.5 FP8 page (dn008.com.cn, section on FP8,
  * steps 1-4) gives the steps. One scale per tensor, fmax = 448 or 57344:
  *
  *   s   = fl32(amax / fmax)            (0 for an all-zero tensor)
@@ -310,7 +310,7 @@ int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* sc
 
 /* ---- FP8 weight-only linear (W8A16) --------------------------------------------
  *
- * The "FP8 weight-only scaled" pipeline of the LongCat avatar comparison page
+ * The FP8 weight-only pipeline of the LongCat avatar comparison page
  * (longcat-avatar-compare.pages.dev, speed overview table): the weight is stored as
  * FP8 codes with per-output-channel scales (fp8_quant_weights_per_channel; a
  * per-tensor scale from fp8_quant_tensor is the same scale repeated n times), the

@@ -3,10 +3,11 @@
 Test infrastructure: part of the CPU oracle (see the package docstring for who
 may import it).
 
-The chain is the one the HunyuanVideo1.5 retrospective (aigcage.com, section 3.1)
-writes out: bf16 activation -> dynamic per-token FP8 quant -> FP8 GEMM -> scale /
-bias / output dtype. The weight is nn.Linear's [N, K] with K contiguous (the
-"column-major B" of that section), so the product is C = A @ W^T.
+The steps follow the HunyuanVideo1.5 retrospective (aigcage.com, section 3.1): the
+bf16 activation is quantised to FP8 with one scale per token, multiplied with the
+FP8 weight, and the product is scaled, biased and converted to the output type. The
+weight is nn.Linear's [N, K] with K contiguous (the column-major B operand of that
+section), so the product is C = A @ W^T.
 
 Exactness of the float64 product: every e4m3fn value is an integer multiple of
 2^-9 with magnitude <= 448, so each product is a multiple of 2^-18 below 2^18 in

@@ -1,11 +1,11 @@
-"""Per-tensor FP8 quantisation and dequantisation (the state-dict converter's "simple scaling").
+"""Per-tensor FP8 quantisation and dequantisation (the state-dict converter's one-scale-per-tensor method).
 
 Test infrastructure: part of the CPU oracle (see the package docstring for who
 may import it).
 
 The QuantizeFP8Format page (runcomfy.com, "Quantize Model to FP8 Format") converts
-every tensor of a state dict to float8_e4m3fn or float8_e5m2 with "a simple scaling
-technique" and gives no formula. The Stable Diffusion 3.5 FP8 page (dn008.com.cn,
+every tensor of a state dict to float8_e4m3fn or float8_e5m2 by scaling it and gives
+no formula. The Stable Diffusion 3.5 FP8 page (dn008.com.cn,
 section on FP8, steps 1-4) gives the steps: the largest magnitude of the tensor,
 a scale from it, x / scale rounded to the 8-bit format, and x_q * scale back in fp32
 at inference. The plainest reading, one scale per tensor:

@@ -4,7 +4,7 @@ Test infrastructure: part of the CPU oracle (see the package docstring for who
 may import it).
 
 The LongCat avatar comparison page (longcat-avatar-compare.pages.dev, speed
-overview table) measures an "FP8 weight-only scaled" pipeline beside the W4A4 one:
+overview table) measures an FP8 weight-only pipeline beside the W4A4 one:
 the weights are stored as FP8 with scales and the activations stay in 16-bit. The
 page gives no formula; the plainest reading, with the per-output-channel weight
 quantisation of the HunyuanVideo1.5 retrospective (aigcage.com, section 2) and
