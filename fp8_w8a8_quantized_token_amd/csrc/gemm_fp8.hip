@@ -195,14 +195,24 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile / wave mismatch");
   static_assert(kRowGroups % kWaves == 0, "fill work must split evenly across waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
-  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS budget of a CU");
-  constexpr int F = kRowGroups / kWaves;  // fills per wave per stage
+  constexpr int kEpiBytes = (BM + 2 * BN) * 4;  // the tile's a_scale, w_scale, bias (fp32)
+  static_assert(STAGES * kStageBytes + kEpiBytes <= 160 * 1024, "LDS budget of a CU");
+  // Which waves issue the DMA fills. A burst of fills stalls the issuing wave at issue
+  // while the texture path drains them, and the matrix core idles if both waves of a
+  // SIMD stall together. With 8 waves (two per SIMD) only waves 0..3, one per SIMD,
+  // issue fills, so each SIMD keeps one wave free to feed its matrix core.
+  constexpr int kFillWaves = kWaves == 8 ? kWaves / 2 : kWaves;
+  constexpr int F = kRowGroups / kFillWaves;   // fills per filling wave per stage
+  constexpr int FA = (BM / RPF) / kFillWaves;  // of which activation rows
+  static_assert(kRowGroups % kFillWaves == 0, "fill work must split evenly across the filling waves");
+  static_assert((BM / RPF) % kFillWaves == 0, "activation fills split evenly across the filling waves");
   static_assert((STAGES - 1) * F < 64, "vmcnt range");
-  static_assert((BM / RPF) % kWaves == 0, "activation fills split evenly across waves");
+  // With two stages of 128-byte k and half the waves filling, a stage's refill goes out
+  // in two halves: the activation rows right after the stage barrier, the weight rows
+  // one MFMA k-step later (they still land before the next barrier).
+  constexpr bool kSplitRefill = STAGES == 2 && H == 2 && kFillWaves < kWaves;
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
-  static_assert((BM + 2 * BN) * 4 <= kStageBytes, "epilogue staging fits in one stage");
   static_assert(!FUSED || STAGES == 2, "the single-launch prologue's fill order assumes two stages");
-  constexpr int FA = (BM / RPF) / kWaves;  // activation fills per wave per stage
 
   auto buf = [](int s) -> uint8_t* {
     switch (s) {
@@ -229,9 +239,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   const v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
   const v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
-  // Epilogue operands of this tile, one value per thread, requested now so their
-  // latency hides behind the k loop.
+  // Epilogue operands of this tile, one value per thread, requested now; they arrive
+  // with the first stage and are parked in LDS, so they hold no registers during the
+  // k loop.
+  float* const epi_sa = reinterpret_cast<float*>(stage_buf<Tag, 7, kEpiBytes>());
+  float* const epi_sw = epi_sa + BM;
+  float* const epi_b = epi_sw + BN;
   const int tid = threadIdx.x;
+  const bool filler = wave < kFillWaves;
   float pre_sa = 0.0f, pre_sw = 0.0f, pre_b = 0.0f;
   if constexpr (!FUSED)
     if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
@@ -244,21 +259,36 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   // lane i writes bytes [16 i, 16 i + 16): row i / CPR of the group, position i % CPR,
   // which holds logical chunk (i % CPR) ^ swz(row). swz depends on row % 16, so with
   // 8-row fills (BK = 128) the chunk differs between even and odd row groups. Tile rows
-  // 0..BM-1 are the activation, BM.. the weight; wave w fills row groups w, w + kWaves, ...
+  // 0..BM-1 are the activation, BM.. the weight; filling wave w fills row groups w,
+  // w + kFillWaves, ...
   const int fr = lane / CPR;
-  const int fchunk0 = (lane % CPR) ^ swz<BK>(fr);            // row group with g * RPF % 16 == 0
-  const int fchunk1 = (lane % CPR) ^ swz<BK>(fr + RPF % 16);  // row group with g * RPF % 16 == 8
-  const uint32_t foff0 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0;
-  const uint32_t foff1 = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1;
+  const int fchunk0_ = (lane % CPR) ^ swz<BK>(fr);            // row group with g * RPF % 16 == 0
+  const int fchunk1_ = (lane % CPR) ^ swz<BK>(fr + RPF % 16);  // row group with g * RPF % 16 == 8
+  const uint32_t foff0_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0_;
+  const uint32_t foff1_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1_;
 
   // part: 0 = the whole stage, 1 = activation rows only, 2 = weight rows only
   auto issue = [&](uint8_t* base, int k0, int part = 0) {
+    if (!filler) return;
+    int fchunk0 = fchunk0_, fchunk1 = fchunk1_;
+    uint32_t foff0 = foff0_, foff1 = foff1_;
+    if constexpr (FUSED) {
+      // formed here from a fresh lane id: kept live across the quantisation phase they
+      // would be spilled, and every refill would wait for the reload
+      int l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      const int r = l / CPR;
+      fchunk0 = (l % CPR) ^ swz<BK>(r);
+      fchunk1 = (l % CPR) ^ swz<BK>(r + RPF % 16);
+      foff0 = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)fchunk0;
+      foff1 = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)fchunk1;
+    }
     const bool kvalid0 = k0 + 16 * fchunk0 < K;
     const bool kvalid1 = k0 + 16 * fchunk1 < K;
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       if ((part == 1 && j >= FA) || (part == 2 && j < FA)) continue;
-      const int g = wave + j * kWaves;
+      const int g = wave + j * kFillWaves;
       const bool odd = ((g * RPF) & 15) != 0;
       const bool kvalid = odd ? kvalid1 : kvalid0;
       const uint32_t foff = odd ? foff1 : foff0;
@@ -345,13 +375,20 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue(buf(s), s * BK, 1);
     // stage 0 is complete once at most the younger stage's activation fills remain
-    if (nst > 1) wait_vm_lgkm0<FA>();
+    if (filler && nst > 1) wait_vm_lgkm0<FA>();
     else wait_vm_lgkm0<0>();
   } else {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue(buf(s), s * BK);
-    wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+    if (filler) wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+    else wait_vm_lgkm0<0>();
+  }
+  // the epilogue operands were requested before the fills: the wait covered them
+  if (tid < BM) epi_sa[tid] = pre_sa;
+  if (tid < BN) {
+    epi_sw[tid] = pre_sw;
+    epi_b[tid] = pre_b;
   }
   block_barrier();
   read_frags(buf(0), 0, f0);
@@ -361,12 +398,15 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     const int t = u / H;
     if (h == H - 1) {
       if (t + 1 < nst) {
-        wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        else wait_vm_lgkm0<0>();
         block_barrier();
-        if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK);
+        if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK, kSplitRefill ? 1 : 0);
       }
       read_frags(buf((s + 1) % STAGES), 0, nxt);
     } else {
+      // the second half of the refill issued at the previous stage barrier
+      if (kSplitRefill && t >= 1 && t + 1 < nst) issue(buf((s + 1) % STAGES), (t + 1) * BK, 2);
       read_frags(buf(s), h + 1, nxt);
     }
     mfma_all(cur);
@@ -382,8 +422,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   }
 
   // Epilogue. The stage buffers are free once every wave has passed this barrier.
-  // 1. Stage the tile's scales and bias in LDS, then pull each lane's share into
-  //    registers (the operand fragments are dead by now).
+  // 1. Pull each lane's share of the tile's scales and bias from LDS into registers
+  //    (the operand fragments are dead by now).
   // 2. Each wave applies them to its accumulators in fp32, rounds once to bf16 and
   //    writes its WTM x WTN tile row-major into its own LDS region (16-byte chunk c of
   //    row r at chunk position c ^ (r % RC)).
@@ -395,17 +435,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(kWavesPerBuf >= 1 && (kWaves + kWavesPerBuf - 1) / kWavesPerBuf <= STAGES,
                 "output staging fits in the stage buffers");
   static_assert(64 % RC == 0 && (WTM * RC) % 64 == 0, "row segments tile the wavefront");
-  float* epi_sa = reinterpret_cast<float*>(buf(0));
-  float* epi_sw = epi_sa + BM;
-  float* epi_b = epi_sw + BN;
-  block_barrier();
-  if (tid < BM) epi_sa[tid] = pre_sa;
-  if (tid < BN) {
-    epi_sw[tid] = pre_sw;
-    epi_b[tid] = pre_b;
-  }
-  wait_vm_lgkm0<63>();  // lgkmcnt(0): the LDS writes are done
-  block_barrier();
   float r_sa[FM];
   float4 r_sw[FN][4], r_b[FN][4];
 #pragma unroll
