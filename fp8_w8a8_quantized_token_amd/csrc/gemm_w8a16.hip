@@ -81,12 +81,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   constexpr int FN = WTN / 32;
   constexpr int kABytes = BM * kARow;
   constexpr int kStageBytes = BM * kARow + BN * kWRow;
-  constexpr int FA = (BM / kARpf) / kWaves;  // activation fills per wave per stage
-  constexpr int FW = (BN / kWRpf) / kWaves;  // weight fills per wave per stage
+  // As in the FP8 GEMM: with 8 waves only waves 0..3 (one per SIMD) issue the DMA
+  // fills, so a wave stalled at fill issue always has a partner that can feed the SIMD's
+  // matrix core.
+  constexpr int kFillWaves = kWaves == 8 ? kWaves / 2 : kWaves;
+  constexpr int FA = (BM / kARpf) / kFillWaves;  // activation fills per filling wave per stage
+  constexpr int FW = (BN / kWRpf) / kFillWaves;  // weight fills per filling wave per stage
   constexpr int F = FA + FW;
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile / wave mismatch");
-  static_assert(FA >= 1 && FW >= 1 && (BM / kARpf) % kWaves == 0 && (BN / kWRpf) % kWaves == 0,
-                "fills split evenly across waves");
+  static_assert(FA >= 1 && FW >= 1 && (BM / kARpf) % kFillWaves == 0 && (BN / kWRpf) % kFillWaves == 0,
+                "fills split evenly across the filling waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS budget of a CU");
   static_assert((STAGES - 1) * F < 64, "vmcnt range");
@@ -138,12 +142,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   const int fwc = (lane % 4) ^ swz<64>(fwr);
   const uint32_t fwoff = (uint32_t)fwr * (uint32_t)K + 16u * (uint32_t)fwc;
 
+  const bool filler = wave < kFillWaves;
   auto issue = [&](uint8_t* base, int s) {
+    if (!filler) return;
     const int ke0 = s * KE;  // first k element of the stage
     const bool va0 = ke0 + 8 * fac0 < K, va1 = ke0 + 8 * fac1 < K;
 #pragma unroll
     for (int j = 0; j < FA; ++j) {
-      const int g = wave + j * kWaves;
+      const int g = wave + j * kFillWaves;
       const bool odd = ((g * kARpf) & 15) != 0;
       const uint32_t vo = (odd ? va1 : va0)
                               ? (uint32_t)(g * kARpf) * (uint32_t)K * 2u + (odd ? faoff1 : faoff0) + (uint32_t)ke0 * 2u
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     const bool vw = ke0 + 16 * fwc < K;
 #pragma unroll
     for (int j = 0; j < FW; ++j) {
-      const int g = wave + j * kWaves;
+      const int g = wave + j * kFillWaves;
       const uint32_t vo = vw ? (uint32_t)(g * kWRpf) * (uint32_t)K + fwoff + (uint32_t)ke0 : kOutOfRange;
       dma16(rsrc_w, (uint32_t)reinterpret_cast<uintptr_t>(base + kABytes + g * 1024), vo);
     }
@@ -212,7 +218,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   for (int s = 0; s < STAGES; ++s)
     if (s < nst) issue(buf(s), s);
   Frags f0, f1;
-  wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+  if (filler) wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+  else wait_vm_lgkm0<0>();
   block_barrier();
   read_frags(buf(0), 0, f0);
 
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     const int t = u / H;
     if (h == H - 1) {
       if (t + 1 < nst) {
-        wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        else wait_vm_lgkm0<0>();
         block_barrier();
         if (t + STAGES < nst) issue(buf(s), t + STAGES);
       }
