@@ -18,13 +18,21 @@ namespace {
 constexpr int kRowsPerBlock = 4;  // one 64-lane wavefront per row
 constexpr int kBlock = 64 * kRowsPerBlock;
 
+// Rows per workgroup of the register-resident kernel: one wavefront per row; rows of
+// 8192 and more go one per workgroup (measured 5-6% faster at [4096 | 32760, 8192] than
+// four per workgroup, equal for shorter rows).
+template <int NC>
+constexpr int rows_per_block() { return NC >= 8 ? 1 : kRowsPerBlock; }
+static_assert(rows_per_block<8>() == 1, "the NC = 8 launch below assumes one row per workgroup");
+
 // NC = number of 16-element chunks each lane keeps in registers (NC * 1024 >= cols).
 template <int NC>
-__global__ __launch_bounds__(kBlock) void quant_rows_regs(const uint16_t* __restrict__ x, int64_t rows,
-                                                         int cols, uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale) {
+__global__ __launch_bounds__(64 * rows_per_block<NC>()) void quant_rows_regs(const uint16_t* __restrict__ x,
+                                                                           int64_t rows, int cols,
+                                                                           uint8_t* __restrict__ q,
+                                                                           float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * rows_per_block<NC>() + (threadIdx.x >> 6);
   if (row >= rows) return;  // uniform across the wavefront
   const int nchunks = cols >> 4;
   uint4 va[NC], vb[NC];
@@ -56,7 +64,8 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint
   else if (chunks_per_lane <= 4)
     quant_rows_regs<4><<<grid, block, 0, stream>>>(x, rows, c, q, scale);
   else if (chunks_per_lane <= 8)
-    quant_rows_regs<8><<<grid, block, 0, stream>>>(x, rows, c, q, scale);
+    quant_rows_regs<8><<<dim3(static_cast<unsigned>(rows)), dim3(64 * rows_per_block<8>()), 0, stream>>>(
+        x, rows, c, q, scale);
   else
     quant_rows_loop<<<grid, block, 0, stream>>>(x, rows, c, q, scale);
   return hipGetLastError();
