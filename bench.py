@@ -336,7 +336,7 @@ def main():
                          "for scaling HBM counter readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(tokens would shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
