@@ -30,6 +30,11 @@ FFN-down linear: GELU (tanh form) of the FFN-up output followed by per-token
 e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
 output, then the plain quantiser), at the FFN-down input [4096, 8192] and at the
 DiT-block size [32760, 8192].
+
+`clocks` reads the shader and memory clocks with amd-smi while the step runs back to
+back, and gives the GEMM's fraction of the dense-FP8 peak at that shader clock
+(256 CUs x 8192 flop per clock) beside `roofline.frac`, which uses the published
+2.4 GHz peak.
 """
 
 import argparse
@@ -37,6 +42,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -49,6 +55,8 @@ M, N, K = 4096, 8192, 2048
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_FLOP_PER_CU_CLK = 8192  # dense FP8 MFMA per CU per shader clock (5.0 PFLOP/s = 256 CUs x 8192 x 2.4 GHz)
+N_CUS = 256
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_ffn_up_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", "gemm_fp8.hip")
 
@@ -56,6 +64,11 @@ GEMM_SOURCE = os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", "gemm_f
 def gemm_bytes(m, n, k):
     # q8 A, q8 W, bf16 out, fp32 a-scale, fp32 w-scale, bf16 bias
     return m * k + n * k + 2 * m * n + 4 * m + 4 * n + 2 * n
+
+
+def pct(sorted_xs, p):
+    """p-th percentile (nearest rank) of an ascending list."""
+    return sorted_xs[min(len(sorted_xs) - 1, max(0, round(p / 100 * (len(sorted_xs) - 1))))]
 
 
 def quant_bytes(m, k):
@@ -129,6 +142,55 @@ def producer_bench(torch, fp8, lib, dev, stream, steps, only_rows=None):
         del xs, q, sc, y
         torch.cuda.empty_cache()
     return out
+
+
+def _smi_clocks(text):
+    """Mean shader and memory clock in MHz from `amd-smi metric --clock --json` (None if absent)."""
+    d = json.loads(text)
+    gpus = d["gpu_data"] if isinstance(d, dict) and "gpu_data" in d else d
+    c = gpus[0]["clock"]
+    gfx = [v["clk"]["value"] for key, v in c.items() if key.startswith("gfx_") and isinstance(v, dict)]
+    mem = [v["clk"]["value"] for key, v in c.items() if key.startswith("mem") and isinstance(v, dict)]
+    mean = lambda xs: round(sum(float(x) for x in xs) / len(xs), 1) if xs else None
+    return mean(gfx), mean(mem)
+
+
+def sample_clocks(torch, step, samples=2, warm_s=0.5):
+    """Shader (SCLK) and memory (MCLK) clocks read with amd-smi while `step` runs back to back.
+
+    The launches go on in this thread while each amd-smi child process runs, so every sample
+    is taken under the timed workload. Returns None when amd-smi is not available."""
+    try:
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(20):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+        gfx, mem = [], []
+        for _ in range(samples):
+            p = subprocess.Popen(["amd-smi", "metric", "--clock", "--json"], stdout=subprocess.PIPE,
+                                 stderr=subprocess.DEVNULL, text=True)
+            t1 = time.perf_counter()
+            while p.poll() is None and time.perf_counter() - t1 < 30:
+                for _ in range(20):
+                    step(i)
+                    i += 1
+                torch.cuda.synchronize()
+            out, _ = p.communicate(timeout=30)
+            g, m = _smi_clocks(out)
+            if g is not None:
+                gfx.append(g)
+            if m is not None:
+                mem.append(m)
+        if not gfx:
+            return None
+        return {"sclk_mhz": round(sum(gfx) / len(gfx), 1),
+                "mclk_mhz": round(sum(mem) / len(mem), 1) if mem else None,
+                "samples": len(gfx), "source": "amd-smi metric --clock (mean over XCDs) during back-to-back steps"}
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        return None
 
 
 def copy_calibration(torch, dev):
@@ -325,6 +387,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock samples")
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
     ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
     ap.add_argument("--no-tensor-quant", action="store_true", help="skip the per-tensor quantisation timing")
@@ -415,6 +478,8 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
 
+    clocks = None if args.no_clocks else sample_clocks(torch, step)
+
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     quant_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
@@ -458,17 +523,27 @@ def main():
             "avg_launch_us": round(g_avg * 1e3, 3),
             "algorithmic_flop_per_launch": flop,
             "algorithmic_bytes_per_launch": gemm_bytes(M, N, K),
+            "p10_launch_us": round(pct(gemm_ms, 10) * 1e3, 3),
+            "median_launch_us": round(pct(gemm_ms, 50) * 1e3, 3),
+            "p90_launch_us": round(pct(gemm_ms, 90) * 1e3, 3),
         },
         "quant": {
             "kernel": "quant_rows_regs",
             "avg_launch_us": round(q_avg * 1e3, 3),
-            "median_launch_us": round(quant_ms[len(quant_ms) // 2] * 1e3, 3),
+            "p10_launch_us": round(pct(quant_ms, 10) * 1e3, 3),
+            "median_launch_us": round(pct(quant_ms, 50) * 1e3, 3),
+            "p90_launch_us": round(pct(quant_ms, 90) * 1e3, 3),
             "gbps": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9, 1),
             "frac_hbm": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes_per_launch": quant_bytes(M, K),
         },
-        "gemm_median_us": round(gemm_ms[len(gemm_ms) // 2] * 1e3, 3),
     }
+    if clocks is not None:
+        # Peak at the clock the chip actually ran: 256 CUs x 8192 FP8 flop per CU per clock.
+        sclk_peak = N_CUS * FP8_FLOP_PER_CU_CLK * clocks["sclk_mhz"] * 1e6 / 1e12
+        clocks["gemm_peak_at_sclk_tflops"] = round(sclk_peak, 1)
+        clocks["gemm_frac_at_sclk"] = round(gemm_tflops / sclk_peak, 4)
+    result["clocks"] = clocks
     del sets
     torch.cuda.empty_cache()
     if not args.no_w8a16:
