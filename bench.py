@@ -12,9 +12,13 @@ total) that no step finds its operands in the 256 MB last-level cache; every
 operand is resident in HBM when the timed region starts.
 
 Prints one JSON line. `value` = 2 M N K / step time (TFLOP/s), from K steps timed
-with events only at the two ends of the region. `roofline` is the GEMM kernel (the
-dominant launch): a second region of K steps records HIP events on the launch
-stream around every launch, giving each kernel's average launch duration.
+with events only at the two ends of the region, after 0.3 s of untimed back-to-back
+steps (`preheat`: the clocks have dropped while the host built the inputs) and the W
+warm-up steps. `roofline` is the GEMM kernel (the
+dominant launch): its average launch duration comes from K launches of the GEMM
+alone, back to back with events on the launch stream at the two ends (likewise
+`quant`); a second region of K steps with an event around every launch gives the
+spread of each kernel's launch duration (`step_events_launch_us`).
 `cpu_baseline` times the CPU oracle (numpy, float64) on the same workload.
 
 `w8a16` (outside the step) times the FP8 weight-only linear (bf16 activation x
@@ -88,6 +92,19 @@ def traffic_from_profile():
         return None
 
 
+def preheat(torch, fn, seconds=0.15, batch=20):
+    """Call fn(i) back to back for about `seconds` (untimed), so a measurement that follows
+    host-side set-up does not start while the clocks ramp up from idle. Returns the calls made."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 PRODUCER_SHAPES = ((4096, 8192, 8), (32760, 8192, 2))  # rows, cols, rotating input sets
 
 
@@ -122,8 +139,7 @@ def producer_bench(torch, fp8, lib, dev, stream, steps, only_rows=None):
 
         res = {}
         for name, fn in (("fused", fused), ("unfused", unfused)):
-            for i in range(5):
-                fn(i)
+            preheat(torch, fn)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
@@ -222,8 +238,7 @@ def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
             from fp8_w8a8_quantized_token_amd import _lib
             raise _lib.Fp8W8A8Error(st, "fp8_w8a16_run")
 
-    for i in range(5):
-        run(i)
+    preheat(torch, run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -232,13 +247,21 @@ def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
-    avg = sum(ts) / len(ts)
+    # average launch duration: the same launches back to back, events only at the ends
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / steps
     tflops = 2.0 * M * N * K / (avg * 1e-3) / 1e12
     cid, tm, tn, wg = sets[0][1].config(M)
     del sets
     torch.cuda.empty_cache()
     return {"kernel": "gemm_w8a16_kernel", "M": M, "N": N, "K": K, "avg_launch_us": round(avg * 1e3, 3),
-            "median_launch_us": round(ts[len(ts) // 2] * 1e3, 3), "achieved": round(tflops, 2),
+            "median_launch_us_events": round(pct(ts, 50) * 1e3, 3), "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "bound": "mfma", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "config": {"id": cid, "tile_m": tm, "tile_n": tn, "workgroups": wg}}
 
@@ -280,8 +303,7 @@ def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
     res = {}
     for name, run in (("two_launch", two), ("single_launch", one), ("two_launch_again", two),
                       ("single_launch_again", one)):
-        for i in range(5):
-            run(i)
+        preheat(torch, run)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -320,8 +342,7 @@ def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
                                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr)
                 if st:
                     raise _lib.Fp8W8A8Error(st, "fp8_quant_tensor")
-            for i in range(3):
-                run(i)
+            preheat(torch, run)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
@@ -386,6 +407,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
+    ap.add_argument("--preheat-s", type=float, default=0.3,
+                    help="seconds of back-to-back steps before the warm-up steps, so the timed steps run at "
+                         "the clocks the chip holds under this load rather than while it ramps up from idle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock samples")
     ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
@@ -456,6 +480,12 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    # Pre-heat: after the host-side set-up the GPU has idled and its clocks have dropped;
+    # without this the first few milliseconds of steps run while they ramp back up.
+    t_pre = time.perf_counter()
+    preheat_steps = preheat(torch, step, args.preheat_s, batch=50)
+    preheat_s = time.perf_counter() - t_pre
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -471,12 +501,69 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region 2: the same K steps with an event on the launch stream around every
-    # launch -> each kernel's average launch duration (the roofline figures).
+    # launch -> the spread (p10 / median / p90) of each kernel's launch duration. An
+    # event between two launches adds its own wait to the interval it closes.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
+
+    # Timed regions 3 and 4: K launches of each kernel alone, back to back over the same
+    # rotating sets, events on the launch stream at the two ends -> each kernel's average
+    # launch duration (the roofline figures; no event sits between two launches).
+    def gemm_only(i):
+        a, q, s, lin, out = sets[i % len(sets)]
+        st = lib.fp8_linear_run(lin._plan, M, ctypes.c_void_p(q.data_ptr()), _lib.A_E4M3,
+                                ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(out.data_ptr()), None, 0, sptr)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
+
+    def quant_only(i, on=sptr):
+        a, q, s, lin, out = sets[i % len(sets)]
+        st = lib.fp8_quant_rows(ctypes.c_void_p(a.data_ptr()), M, K, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(s.data_ptr()), on)
+        if st:
+            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
+
+    def graph_avg(fn):
+        """K launches captured in one HIP graph, replayed with events at its two ends: the
+        quantiser's launches are short enough that eager launches from Python leave the GPU
+        waiting on the host between them."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(0, ctypes.c_void_p(side.cuda_stream))
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            for i in range(args.steps):
+                fn(i, cap)
+        torch.cuda.synchronize()
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / args.steps
+
+    def back_to_back(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    g_avg = back_to_back(gemm_only)
+    q_avg_eager = back_to_back(quant_only)
+    q_avg = graph_avg(quant_only)
 
     clocks = None if args.no_clocks else sample_clocks(torch, step)
 
@@ -484,8 +571,6 @@ def main():
     ms_per_step = total_ms / args.steps
     quant_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     gemm_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    q_avg = sum(quant_ms) / len(quant_ms)
-    g_avg = sum(gemm_ms) / len(gemm_ms)
     flop = 2.0 * M * N * K
     value = flop / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flop / (g_avg * 1e-3) / 1e12
@@ -498,6 +583,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "preheat": {"seconds": round(preheat_s, 3), "steps": preheat_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -523,16 +609,19 @@ def main():
             "avg_launch_us": round(g_avg * 1e3, 3),
             "algorithmic_flop_per_launch": flop,
             "algorithmic_bytes_per_launch": gemm_bytes(M, N, K),
-            "p10_launch_us": round(pct(gemm_ms, 10) * 1e3, 3),
-            "median_launch_us": round(pct(gemm_ms, 50) * 1e3, 3),
-            "p90_launch_us": round(pct(gemm_ms, 90) * 1e3, 3),
+            "step_events_launch_us": {"avg": round(sum(gemm_ms) / len(gemm_ms) * 1e3, 3),
+                                      "p10": round(pct(gemm_ms, 10) * 1e3, 3),
+                                      "median": round(pct(gemm_ms, 50) * 1e3, 3),
+                                      "p90": round(pct(gemm_ms, 90) * 1e3, 3)},
         },
         "quant": {
             "kernel": "quant_rows_regs",
             "avg_launch_us": round(q_avg * 1e3, 3),
-            "p10_launch_us": round(pct(quant_ms, 10) * 1e3, 3),
-            "median_launch_us": round(pct(quant_ms, 50) * 1e3, 3),
-            "p90_launch_us": round(pct(quant_ms, 90) * 1e3, 3),
+            "avg_launch_us_eager_back_to_back": round(q_avg_eager * 1e3, 3),
+            "step_events_launch_us": {"avg": round(sum(quant_ms) / len(quant_ms) * 1e3, 3),
+                                      "p10": round(pct(quant_ms, 10) * 1e3, 3),
+                                      "median": round(pct(quant_ms, 50) * 1e3, 3),
+                                      "p90": round(pct(quant_ms, 90) * 1e3, 3)},
             "gbps": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9, 1),
             "frac_hbm": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes_per_launch": quant_bytes(M, K),

@@ -3,6 +3,8 @@
     python -m fp8_w8a8_quantized_token_amd.profiling stats <kernel_stats.csv> --command "<cmd>" [--out file.md]
     python -m fp8_w8a8_quantized_token_amd.profiling traffic <fetch counter csv> <write counter csv>
         --kernel <substring> --command "<cmd>" [--out file.md] [--json file.json]
+    python -m fp8_w8a8_quantized_token_amd.profiling runs <kernel_trace.csv> --kernel <substring>
+        [--after <substring>] [--min-run N]
 
 ``stats`` renders rocprofv3's ``--kernel-trace --stats`` table (calls, average and
 min/max duration per kernel). ``traffic`` turns ``--pmc FETCH_SIZE`` and
@@ -10,6 +12,11 @@ min/max duration per kernel). ``traffic`` turns ``--pmc FETCH_SIZE`` and
 the same counters read for a plain 1 GiB device copy in the same run (the bench's
 ``--copy-calibration`` launches), and records the SHA-256 of the GEMM source the
 counters were taken on so that stale figures are not reported as current.
+``runs`` reads ``--kernel-trace`` records and lists the stretches in which one kernel
+ran back to back (at least ``--min-run`` launches in a row), or, with ``--after``,
+the stretches in which it directly followed another kernel each time (a two-kernel
+step), with the kernel's mean and median duration and the mean idle gap before it:
+so one region of a benchmark can be matched with its kernel-trace durations.
 """
 
 import argparse
@@ -112,6 +119,38 @@ def traffic_markdown(t, command, algorithmic=None):
     return "\n".join(out) + "\n"
 
 
+def runs(trace_csv, kernel, after=None, min_run=100):
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    start = [int(r["Start_Timestamp"]) for r in rows]
+    end = [int(r["End_Timestamp"]) for r in rows]
+    # indices of the launches of interest and the launch each one must follow
+    stride = 2 if after else 1
+    hits = [i for i in range(1, len(rows))
+            if kernel in names[i] and (after in names[i - 1] if after else kernel in names[i - 1])]
+    out, cur = [], []
+    for i in hits + [None]:
+        if cur and (i is None or i - cur[-1] != stride):
+            if len(cur) >= min_run:
+                d = [(end[k] - start[k]) / 1e3 for k in cur]
+                gap = [(start[k] - end[k - 1]) / 1e3 for k in cur]
+                out.append({"launches": len(cur), "mean_us": statistics.mean(d), "median_us": statistics.median(d),
+                            "mean_gap_before_us": statistics.mean(gap)})
+            cur = []
+        if i is not None:
+            cur.append(i)
+    return out
+
+
+def runs_markdown(found, kernel, after, command):
+    what = f"`{kernel}` launches each directly after `{after}`" if after else f"`{kernel}` launches back to back"
+    out = [f"Stretches of {what}:", "", "| launches | mean us | median us | mean idle gap before us |",
+           "|---|---|---|---|"]
+    for r in found:
+        out.append(f"| {r['launches']} | {r['mean_us']:.2f} | {r['median_us']:.2f} | {r['mean_gap_before_us']:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -128,9 +167,19 @@ def main(argv=None):
     b.add_argument("--source", default=GEMM_SOURCE, help="the kernel's source file, hashed into the record")
     b.add_argument("--out")
     b.add_argument("--json")
+    c = sub.add_parser("runs")
+    c.add_argument("csv")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--after")
+    c.add_argument("--min-run", type=int, default=100)
+    c.add_argument("--command", default="")
+    c.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         text = stats_markdown(args.csv, args.command)
+    elif args.cmd == "runs":
+        text = runs_markdown(runs(args.csv, args.kernel, args.after, args.min_run), args.kernel, args.after,
+                             args.command)
     else:
         t = traffic(args.fetch_csv, args.write_csv, args.kernel, args.source)
         text = traffic_markdown(t, args.command, args.algorithmic)
