@@ -35,6 +35,10 @@ e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
 output, then the plain quantiser), at the FFN-down input [4096, 8192] and at the
 DiT-block size [32760, 8192].
 
+`configs` (outside the step) times the QKV config (one quantisation of the [32760,
+2048] hidden input, three GEMMs, the 26-row encoder input through the same weights)
+and the DiT block (4 quantisations, 6 GEMMs at 32760 tokens) as whole steps.
+
 `clocks` reads the shader and memory clocks with amd-smi while the step runs back to
 back, and gives the GEMM's fraction of the dense-FP8 peak at that shader clock
 (256 CUs x 8192 flop per clock) beside `roofline.frac`, which uses the published
@@ -324,6 +328,57 @@ def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
             "speedup": round(two_us / one_us, 4)}
 
 
+def block_bench(torch, fp8, lib, dev, stream, steps, config):
+    """A whole synthetic config as one step: each activation quantised once per token, then
+    every linear that reads it (QKV: one quantisation, three GEMMs, plus the 26-row encoder
+    input through the same three weights; DiT block: 4 quantisations, 6 GEMMs)."""
+    from fp8_w8a8_quantized_token_amd import _lib
+    from workloads.synth import layer_specs, make_config
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    cfg = make_config(config)
+    acts = {name: a.to(dev) for name, a in cfg["activations"].items()}
+    codes = {name: (torch.empty(a.shape, dtype=torch.uint8, device=dev),
+                    torch.empty((a.shape[0],), dtype=torch.float32, device=dev)) for name, a in acts.items()}
+    lins, outs, flop = {}, {}, 0.0
+    for layer, act, m, n, k in layer_specs(config):
+        lins[layer] = fp8.Fp8Linear(cfg["weights"][layer].to(dev), cfg["biases"][layer].to(dev))
+        outs[layer] = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        flop += 2.0 * m * n * k
+    del cfg
+    order = [(name, [(layer, act_m) for layer, act, act_m, _, _ in layer_specs(config) if act == name])
+             for name in acts]
+
+    def step(_i):
+        for name, layers in order:
+            a = acts[name]
+            q, sc = codes[name]
+            st = lib.fp8_quant_rows(p(a), a.shape[0], a.shape[1], p(q), p(sc), sptr)
+            if st:
+                raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
+            for layer, m in layers:
+                st = lib.fp8_linear_run(lins[layer]._plan, m, p(q), _lib.A_E4M3, p(sc), p(outs[layer]), None, 0,
+                                        sptr)
+                if st:
+                    raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
+
+    preheat(torch, step, batch=5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = {"quantisations": len(order), "gemms": len(lins), "steps": steps, "flop_per_step": flop,
+           "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+           "gemm_configs": {layer: lin.config(outs[layer].shape[0])[0] for layer, lin in lins.items()}}
+    del acts, codes, lins, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
     """Per-tensor quantisation (both formats): two launches, HBM-resident rotating inputs."""
     from fp8_w8a8_quantized_token_amd import _lib
@@ -416,6 +471,7 @@ def main():
     ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
     ap.add_argument("--no-tensor-quant", action="store_true", help="skip the per-tensor quantisation timing")
     ap.add_argument("--no-quant-gemm", action="store_true", help="skip the single-launch quant + GEMM timing")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the whole-config (QKV, DiT block) timings")
     ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
                     help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -643,6 +699,9 @@ def main():
         result["tensor_quant"] = tensor_quant_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 50)))
     if not args.no_quant_gemm:
         result["quant_gemm"] = quant_gemm_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
+    if not args.no_blocks:
+        result["configs"] = {name: block_bench(torch, fp8, lib, dev, stream, max(5, min(args.steps, 20)), name)
+                             for name in ("qkv", "dit_block")}
     if args.copy_calibration:
         copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}
