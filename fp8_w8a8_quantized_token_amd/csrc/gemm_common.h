@@ -41,9 +41,14 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) 
                : "memory");
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even), lo in bits 0..15. Converted as one
+// two-element vector so that a single v_cvt_pk_bf16_f32 does both: converting the two
+// values one by one costs two converts plus a shift and an OR.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // v_cvt_pk_bf16_f32: round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf16));
 }
 
 // Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin (id % 8);
