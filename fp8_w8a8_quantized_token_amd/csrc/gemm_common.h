@@ -1,5 +1,5 @@
 // Building blocks shared by the GEMM kernels (FP8 x FP8 and bf16 x FP8) for gfx950:
-// buffer descriptors, global -> LDS DMA, bf16 packing, the XCD-aware tile order,
+// buffer descriptors, global -> LDS DMA, bf16 packing, the output-tile store, the XCD-aware tile order,
 // per-stage LDS objects, precise waits, the MFMA / LDS-read interleave and the LDS
 // chunk swizzle. Each translation unit that includes it gets its own copy.
 #pragma once
@@ -12,6 +12,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -49,6 +50,34 @@ typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 // values one by one costs two converts plus a shift and an OR.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf16));
+}
+
+// Store a wave's bf16 output tile, staged in LDS at `wout` (WTM rows of RC 16-byte chunks,
+// chunk c of row r at position c ^ (r % RC)), to out[row0 + r][col0 + 8 c ...] of an
+// m x n row-major bf16 matrix. Each store writes 64 / RC whole rows of the wave tile, 16
+// bytes per lane. The buffer descriptor covers exactly the tile's valid rows, so rows
+// past m fall outside it and are dropped, and lanes whose 8 columns lie past n are
+// pointed out of range: no per-store bounds test.
+template <int WTM, int RC>
+__device__ __forceinline__ void store_wave_tile(const uint8_t* wout, int lane, uint16_t* out, int m, int n,
+                                                int row0, int col0) {
+  constexpr int kRowsPerStore = 64 / RC;
+  static_assert(64 % RC == 0 && WTM % kRowsPerStore == 0, "row segments tile the wavefront");
+  const int rows_valid = min(WTM, m - row0);
+  if (rows_valid <= 0) return;
+  const uint32_t row_bytes = (uint32_t)n * 2u;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      out + (int64_t)row0 * n, 0, (uint32_t)rows_valid * row_bytes, kBufferConfig);
+  const int c = lane % RC;
+  const int ncol = col0 + c * 8;
+  const uint32_t voff = ncol < n ? (uint32_t)(lane / RC) * row_bytes + (uint32_t)ncol * 2u : kOutOfRange;
+#pragma unroll
+  for (int t = 0; t < WTM / kRowsPerStore; ++t) {
+    const int r = t * kRowsPerStore + lane / RC;
+    const uint4 v = *reinterpret_cast<const uint4*>(wout + r * (RC * 16) + ((c ^ (r % RC)) << 4));
+    const v4u data = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(data, rsrc, voff + (uint32_t)(t * kRowsPerStore) * row_bytes, 0, 0);
+  }
 }
 
 // Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin (id % 8);

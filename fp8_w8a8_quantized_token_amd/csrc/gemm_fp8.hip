@@ -73,8 +73,6 @@ struct GemmArgs {
 constexpr int kScDevice = 16;  // cache-policy bit sc1: device-scope coherent access
 constexpr uint64_t kStealAfterTicks = 10000;  // 100 us of the 100 MHz real-time clock
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
 // Per-token results of the single-launch form are stored with device scope (sc1):
 // written through the XCD's L2 to the device coherence point, and counted complete
 // (vmcnt) only once visible there. A workgroup that has waited for its own stores can
@@ -474,17 +472,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     }
   }
   // own region only: LDS executes one wave's accesses in order, no barrier needed
-  const int64_t N = args.n;
-  constexpr int kRowsPerStore = 64 / RC;
-#pragma unroll
-  for (int t = 0; t < WTM / kRowsPerStore; ++t) {
-    const int r = t * kRowsPerStore + lane / RC;
-    const int c = lane % RC;
-    const uint4 v = *reinterpret_cast<const uint4*>(wout + r * (RC * 16) + ((c ^ (r % RC)) << 4));
-    const int m = m0 + wm * WTM + r;
-    const int n = n0 + wn * WTN + c * 8;
-    if (m < args.m && n < args.n) *reinterpret_cast<uint4*>(args.out + (int64_t)m * N + n) = v;
-  }
+  store_wave_tile<WTM, RC>(wout, lane, args.out, args.m, args.n, m0 + wm * WTM, n0 + wn * WTN);
 }
 
 template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false>

@@ -301,17 +301,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
       }
     }
   }
-  const int64_t N = args.n;
-  constexpr int kRowsPerStore = 64 / RC;
-#pragma unroll
-  for (int t = 0; t < WTM / kRowsPerStore; ++t) {
-    const int r = t * kRowsPerStore + lane / RC;
-    const int c = lane % RC;
-    const uint4 v = *reinterpret_cast<const uint4*>(wout + r * (RC * 16) + ((c ^ (r % RC)) << 4));
-    const int m = m0 + wm * WTM + r;
-    const int n = n0 + wn * WTN + c * 8;
-    if (m < args.m && n < args.n) *reinterpret_cast<uint4*>(args.out + (int64_t)m * N + n) = v;
-  }
+  // own region only: LDS executes one wave's accesses in order, no barrier needed
+  store_wave_tile<WTM, RC>(wout, lane, args.out, args.m, args.n, m0 + wm * WTM, n0 + wn * WTN);
 }
 
 template <int BM, int BN, int WM, int WN, int S, int GM, int FMT>
