@@ -28,7 +28,17 @@ import statistics
 import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCE = os.path.join(PKG_DIR, "csrc", "gemm_fp8.hip")
+# the FP8 GEMM kernel's sources: the kernel and the building blocks it includes
+GEMM_SOURCES = [os.path.join(PKG_DIR, "csrc", "gemm_fp8.hip"), os.path.join(PKG_DIR, "csrc", "gemm_common.h")]
+
+
+def sources_sha256(paths):
+    """SHA-256 over the files' bytes, in the order given."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 CALIBRATION_BYTES = 1 << 30  # the bench's copy calibration moves 1 GiB per launch
 
 
@@ -68,7 +78,7 @@ def _calibration(per):
     return statistics.median(vals)
 
 
-def traffic(fetch_csv, write_csv, kernel, source=GEMM_SOURCE):
+def traffic(fetch_csv, write_csv, kernel, sources=GEMM_SOURCES):
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
     write = _per_kernel(write_csv, "WRITE_SIZE")
     cal_fetch = _calibration(fetch)
@@ -93,10 +103,10 @@ def traffic(fetch_csv, write_csv, kernel, source=GEMM_SOURCE):
         "fetch_bytes_per_launch": fetch_bytes,
         "write_bytes_per_launch": write_bytes,
         "hbm_bytes_per_launch": fetch_bytes + write_bytes,
-        "source": os.path.relpath(source, os.path.dirname(PKG_DIR)),
-        "source_sha256": hashlib.sha256(open(source, "rb").read()).hexdigest(),
-        # kept under its historical key for the GEMM (the bench reads it)
-        "gemm_source_sha256": hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest(),
+        "source": [os.path.relpath(p, os.path.dirname(PKG_DIR)) for p in sources],
+        "source_sha256": sources_sha256(sources),
+        # the FP8 GEMM's sources at measurement (the bench reports the traffic only while they match)
+        "gemm_source_sha256": sources_sha256(GEMM_SOURCES),
     }
 
 
@@ -115,7 +125,8 @@ def traffic_markdown(t, command, algorithmic=None):
     if algorithmic:
         out.append(f"| algorithmic bytes / launch | {algorithmic / 1e6:.2f} MB |")
         out.append(f"| traffic / algorithmic | {t['hbm_bytes_per_launch'] / algorithmic:.2f} |")
-    out += ["", f"Kernel source `{t['source']}` SHA-256 at measurement: `{t['source_sha256']}`"]
+    src = t["source"] if isinstance(t["source"], str) else " + ".join(t["source"])
+    out += ["", f"Kernel source `{src}` SHA-256 at measurement: `{t['source_sha256']}`"]
     return "\n".join(out) + "\n"
 
 
@@ -164,7 +175,8 @@ def main(argv=None):
     b.add_argument("--kernel", required=True)
     b.add_argument("--command", required=True)
     b.add_argument("--algorithmic", type=float)
-    b.add_argument("--source", default=GEMM_SOURCE, help="the kernel's source file, hashed into the record")
+    b.add_argument("--source", nargs="+", default=GEMM_SOURCES,
+                   help="the kernel's source files, hashed (in this order) into the record")
     b.add_argument("--out")
     b.add_argument("--json")
     c = sub.add_parser("runs")
