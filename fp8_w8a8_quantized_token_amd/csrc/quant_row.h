@@ -1,8 +1,10 @@
 // Per-row e4m3fn quantisation of bf16 values held in registers, shared by the plain
 // per-token quantiser and the activation producers that emit FP8.
 //
-// One 64-lane wavefront owns a row; each lane holds 16 consecutive bf16 per chunk
-// (two uint4). The row maximum is a butterfly over the wavefront, the scale is
+// One 64-lane wavefront owns a row (or a share of it, when a workgroup splits long rows
+// over several wavefronts); each lane holds 16 consecutive bf16 per chunk (two uint4).
+// The row maximum is a butterfly over the wavefront (and across the wavefronts of a
+// split row, an exchange the caller does), the scale is
 // s = fl32(amax / 448), and each element becomes the e4m3fn code of the correctly
 // rounded fp32 quotient x / s (HunyuanVideo1.5 BF16->FP8 retrospective,
 // aigcage.com, section 3.1; the 448 denominator is the largest finite e4m3fn).
@@ -80,14 +82,16 @@ __device__ __forceinline__ float absmax16(float m, const uint4& a, const uint4& 
   return m;
 }
 
-// Load a row's chunks c = j * 64 + lane (j < NC) into registers; chunks past the
-// row read as zeros (they never raise the maximum and are never stored).
-template <int NC>
+// Load a row's chunks into registers: with the row split over WPR wavefronts, wavefront
+// `part` holds chunks c = (j * WPR + part) * 64 + lane (j < NC); one wavefront per row
+// (WPR = 1) holds c = j * 64 + lane. Chunks past the row read as zeros (they never raise
+// the maximum and are never stored).
+template <int NC, int WPR = 1>
 __device__ __forceinline__ void load_row(const uint16_t* xr, int nchunks, int lane, uint4 (&va)[NC],
-                                         uint4 (&vb)[NC]) {
+                                         uint4 (&vb)[NC], int part = 0) {
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int c = j * 64 + lane;
+    const int c = (j * WPR + part) * 64 + lane;
     if (c < nchunks) {
       const uint4* p = reinterpret_cast<const uint4*>(xr + static_cast<int64_t>(c) * 16);
       va[j] = p[0];
@@ -110,20 +114,27 @@ struct PlainStore {
   __device__ __forceinline__ void scale(float* srow, float s) const { *srow = s; }
 };
 
-// Scale and codes of a register-resident row (every lane of the wavefront calls it).
-template <int NC, class Store = PlainStore>
-__device__ __forceinline__ void quant_row(const uint4 (&va)[NC], const uint4 (&vb)[NC], int nchunks, int lane,
-                                          uint8_t* qr, float* srow, const Store& st = Store{}) {
+// Largest magnitude among the chunks this lane holds (0 for none).
+template <int NC>
+__device__ __forceinline__ float lane_absmax(const uint4 (&va)[NC], const uint4 (&vb)[NC]) {
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NC; ++j) amax = absmax16(amax, va[j], vb[j]);
-  amax = wave_max(amax);
+  return amax;
+}
+
+// Scale and codes of the chunks one wavefront holds (loaded by load_row<NC, WPR> as
+// `part`), given the whole row's maximum `amax`. Wavefront 0's lane 0 stores the scale.
+template <int NC, int WPR = 1, class Store = PlainStore>
+__device__ __forceinline__ void quant_row_part(const uint4 (&va)[NC], const uint4 (&vb)[NC], int nchunks,
+                                               int lane, int part, float amax, uint8_t* qr, float* srow,
+                                               const Store& st = Store{}) {
   const float s = amax / 448.0f;
-  if (lane == 0) st.scale(srow, s);
+  if (lane == 0 && part == 0) st.scale(srow, s);
 
 #define FP8W8A8_QUANT_STORE(MODE, R)                                                     \
   _Pragma("unroll") for (int j = 0; j < NC; ++j) {                                       \
-    const int c = j * 64 + lane;                                                         \
+    const int c = (j * WPR + part) * 64 + lane;                                          \
     if (c < nchunks) st.codes(qr, c, nchunks, quant16<MODE>(va[j], vb[j], s, R));        \
   }
   if (amax >= kTinyAmax) {
@@ -135,6 +146,13 @@ __device__ __forceinline__ void quant_row(const uint4 (&va)[NC], const uint4 (&v
     FP8W8A8_QUANT_STORE(Mode::kExact, 0.0f)
   }
 #undef FP8W8A8_QUANT_STORE
+}
+
+// Scale and codes of a register-resident row (every lane of the wavefront calls it).
+template <int NC, class Store = PlainStore>
+__device__ __forceinline__ void quant_row(const uint4 (&va)[NC], const uint4 (&vb)[NC], int nchunks, int lane,
+                                          uint8_t* qr, float* srow, const Store& st = Store{}) {
+  quant_row_part<NC, 1, Store>(va, vb, nchunks, lane, 0, wave_max(lane_absmax<NC>(va, vb)), qr, srow, st);
 }
 
 // Identity map of a chunk (the plain quantiser).

@@ -56,7 +56,7 @@ def test_large_config_activations_sampled_rows(config):
 
 
 @pytest.mark.parametrize("rows", [1, 3, 63, 65, 257])
-@pytest.mark.parametrize("cols", [16, 48, 272, 1024, 1040, 2064, 8192, 8208, 16400, 65536])
+@pytest.mark.parametrize("cols", [16, 48, 272, 1024, 1040, 2064, 4096, 4112, 8192, 8208, 16400, 65536])
 def test_edge_shapes(rows, cols):
     if rows * cols > 257 * 16400:
         rows = 3
