@@ -33,7 +33,6 @@ namespace {
 constexpr int kTableEntries = 1 << 16;
 constexpr int kWaves = 16;  // per workgroup; one workgroup per CU (the table fills LDS)
 constexpr int kBlock = 64 * kWaves;
-constexpr int kWavesWideRows = 8;  // rows of 8 chunks per lane need 2 waves/SIMD of registers
 
 // ---- table construction --------------------------------------------------------
 
@@ -163,6 +162,59 @@ __global__ __launch_bounds__(64 * WAVES) void act_quant_rows_regs(const uint16_t
   }
 }
 
+// Fused producer for rows of 4097..8192 elements: each row split over 4 wavefronts (NC
+// chunks per lane), 4 rows in flight per 16-wavefront workgroup, and the next row's
+// loads issued before the current row is mapped, so every wavefront keeps a row in
+// flight while it works through the table lookups. The 4 wavefront maxima of a row meet
+// in LDS (double-buffered by iteration, one barrier per iteration); every wavefront of
+// the workgroup runs the same iterations, so the barrier count matches.
+constexpr int kSplit = 4;                  // wavefronts per row
+constexpr int kSlots = kWaves / kSplit;    // rows in flight per workgroup
+template <int NC>
+__global__ __launch_bounds__(kBlock) void act_quant_rows_split(const uint16_t* __restrict__ x, int64_t rows,
+                                                              int cols, const uint16_t* __restrict__ table,
+                                                              uint8_t* __restrict__ q, float* __restrict__ scale) {
+  uint16_t* lut = shared_table();
+  __shared__ float wave_amax[2][kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = wave / kSplit, part = wave % kSplit;
+  const int nchunks = cols >> 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kSlots;
+  int64_t base = static_cast<int64_t>(blockIdx.x) * kSlots;
+  uint4 va[NC], vb[NC], na[NC] = {}, nb[NC] = {};
+  if (base + slot < rows) qrow::load_row<NC, kSplit>(x + (base + slot) * cols, nchunks, lane, va, vb, part);
+  stage_table(table, lut);
+  __syncthreads();
+  const LutMap map{lut};
+  for (int it = 0; base < rows; base += stride, ++it) {
+    const int64_t row = base + slot, next = row + stride;
+    if (next < rows) qrow::load_row<NC, kSplit>(x + next * cols, nchunks, lane, na, nb, part);
+    float m = 0.0f;
+    if (row < rows) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        map(va[j]);
+        map(vb[j]);
+      }
+      m = qrow::wave_max(qrow::lane_absmax<NC>(va, vb));
+    }
+    if (lane == 0) wave_amax[it & 1][wave] = m;
+    __syncthreads();
+    if (row < rows) {
+      float amax = wave_amax[it & 1][slot * kSplit];
+#pragma unroll
+      for (int i = 1; i < kSplit; ++i) amax = fmaxf(amax, wave_amax[it & 1][slot * kSplit + i]);
+      qrow::quant_row_part<NC, kSplit>(va, vb, nchunks, lane, part, amax, q + row * cols, scale + row);
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      va[j] = na[j];
+      vb[j] = nb[j];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void act_quant_rows_loop(const uint16_t* __restrict__ x, int64_t rows, int cols,
                                                              const uint16_t* __restrict__ table,
                                                              uint8_t* __restrict__ q, float* __restrict__ scale) {
@@ -231,8 +283,8 @@ hipError_t launch_act_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, 
   } else if (chunks_per_lane <= 4) {
     act_quant_rows_regs<4, kWaves><<<grid, block, 0, stream>>>(x, rows, c, table, q, scale);
   } else if (chunks_per_lane <= 8) {
-    const dim3 g8(static_cast<unsigned>(producer_grid(rows, kWavesWideRows, cus))), b8(64 * kWavesWideRows);
-    act_quant_rows_regs<8, kWavesWideRows><<<g8, b8, 0, stream>>>(x, rows, c, table, q, scale);
+    const dim3 gs(static_cast<unsigned>(producer_grid(rows, kSlots, cus)));
+    act_quant_rows_split<2><<<gs, block, 0, stream>>>(x, rows, c, table, q, scale);
   } else {
     act_quant_rows_loop<<<grid, block, 0, stream>>>(x, rows, c, table, q, scale);
   }
