@@ -301,6 +301,31 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     }
   };
 
+  // The first stages' fills, before any wave has MFMA work to keep fed, come from every
+  // wave: FW per wave per stage instead of F from each filling wave.
+  constexpr int FW = kRowGroups / kWaves;
+  constexpr int FAW = (BM / RPF) / kWaves;
+  static_assert(kRowGroups % kWaves == 0 && (BM / RPF) % kWaves == 0, "prologue fills split evenly");
+  auto issue_all = [&](uint8_t* base, int k0) {
+    const bool kvalid0 = k0 + 16 * fchunk0_ < K;
+    const bool kvalid1 = k0 + 16 * fchunk1_ < K;
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      const int g = wave + j * kWaves;
+      const bool odd = ((g * RPF) & 15) != 0;
+      const bool kvalid = odd ? kvalid1 : kvalid0;
+      const uint32_t foff = odd ? foff1_ : foff0_;
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
+      if (j < FAW) {
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        dma16(rsrc_a, dst, vo);
+      } else {
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        dma16(rsrc_w, dst, vo);
+      }
+    }
+  };
+
   // Operand reads for the 32x32x64 MFMA k-step h of a stage: lane l holds row l % 32 of
   // a 32-row fragment, k bytes 64 h + [32 (l/32), +32) = logical chunks
   // 4 h + 2 (l/32) and 4 h + 2 (l/32) + 1.
@@ -375,6 +400,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     // stage 0 is complete once at most the younger stage's activation fills remain
     if (filler && nst > 1) wait_vm_lgkm0<FA>();
     else wait_vm_lgkm0<0>();
+  } else if constexpr (kFillWaves < kWaves && STAGES == 2) {
+    // (two stages only: the first stage boundary then waits for every fill in flight,
+    // whichever wave issued it)
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue_all(buf(s), s * BK);
+    wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
   } else {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
