@@ -303,6 +303,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
 
   // The first stages' fills, before any wave has MFMA work to keep fed, come from every
   // wave: FW per wave per stage instead of F from each filling wave.
+  constexpr bool kPrologueAll = !FUSED && kFillWaves < kWaves;
   constexpr int FW = kRowGroups / kWaves;
   constexpr int FAW = (BM / RPF) / kWaves;
   static_assert(kRowGroups % kWaves == 0 && (BM / RPF) % kWaves == 0, "prologue fills split evenly");
@@ -400,9 +401,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     // stage 0 is complete once at most the younger stage's activation fills remain
     if (filler && nst > 1) wait_vm_lgkm0<FA>();
     else wait_vm_lgkm0<0>();
-  } else if constexpr (kFillWaves < kWaves && STAGES == 2) {
-    // (two stages only: the first stage boundary then waits for every fill in flight,
-    // whichever wave issued it)
+  } else if constexpr (kPrologueAll) {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue_all(buf(s), s * BK);
@@ -428,7 +427,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     const int t = u / H;
     if (h == H - 1) {
       if (t + 1 < nst) {
-        if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        // stage t + 1 complete: the first stages came from every wave (FW each), later
+        // ones from the filling waves (F each)
+        if (kPrologueAll && t == 0) wait_stage<FW, STAGES>(min(nst - 2, STAGES - 2));
+        else if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
         else wait_vm_lgkm0<0>();
         block_barrier();
         if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK, kSplitRefill ? 1 : 0);
