@@ -95,6 +95,38 @@ int check_weight_args(int64_t n, int64_t k, const void* w, const float* w_scale,
   return FP8W8A8_OK;
 }
 
+// Relative throughput of one workgroup of each configuration, with one workgroup on a
+// CU (eff1) and with two or more sharing it (eff2), and how many of its workgroups can
+// share a CU (LDS / register bound). The two families order their configurations the
+// same way: 256 x 256, 256 x 128, 128 x 256, 128 x 128 (4 waves), 64 x 64 (4 waves).
+struct TileModel {
+  double eff1, eff2;
+  int per_cu;
+};
+// FP8 GEMM, measured on MI355X (the configurations interleaved in one process, 17 shapes
+// from 26 x 2048 x 2048 to 32760 x 2048 x 8192): 128 x 256 is at least as fast as
+// 256 x 128 wherever both apply (up to 11% faster at 4096 x 2048 x 2048 and
+// 1024 x 8192 x 2048), and a lone 4-wave 128 x 128 workgroup on a CU (one wave per SIMD)
+// runs at about half its rate with two sharing the CU.
+TileModel w8a8_tile_model(int config) {
+  switch (config) {
+    case 0: return {1.00, 1.00, 1};
+    case 1: return {0.95, 0.95, 1};
+    case 2: return {0.96, 0.96, 1};
+    case 3: return {0.45, 0.85, 2};
+    default: return {0.40, 0.40, 3};
+  }
+}
+TileModel w8a16_tile_model(int config) {
+  switch (config) {
+    case 0: return {1.00, 1.00, 1};
+    case 1: return {0.96, 0.96, 1};
+    case 2: return {0.96, 0.96, 1};
+    case 3: return {0.75, 0.75, 2};
+    default: return {0.40, 0.40, 3};
+  }
+}
+
 // A family of compiled GEMM configurations (the W8A8 GEMM, the W8A16 GEMM) as the
 // selector sees it.
 struct Family {
@@ -102,43 +134,25 @@ struct Family {
   const GemmConfig* (*config)(int);
   int64_t (*workgroups)(int, int64_t, int64_t);
   int (*threads)(int);
+  TileModel (*model)(int);
 };
-const Family kW8A8{gemm_config_count, gemm_config, gemm_workgroups, gemm_threads};
-const Family kW8A16{w8a16_config_count, w8a16_config, w8a16_workgroups, w8a16_threads};
+const Family kW8A8{gemm_config_count, gemm_config, gemm_workgroups, gemm_threads, w8a8_tile_model};
+const Family kW8A16{w8a16_config_count, w8a16_config, w8a16_workgroups, w8a16_threads, w8a16_tile_model};
 
 bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
   return f.workgroups(config, m, n) * f.threads(config) < kMaxGridThreads;
 }
 bool grid_fits(int config, int64_t m, int64_t n) { return grid_fits(kW8A8, config, m, n); }
 
-// Relative throughput of one workgroup of each configuration when it has a CU to
-// itself, and how many of its workgroups share a CU (LDS / register bound). Measured
-// on MI355X: the 256 x 256 tiles run at the highest per-CU rate, 256 x 128 and
-// 128 x 256 close to it, the 4-wave 128 x 128 and 64 x 64 tiles well below. Both
-// families order their configurations the same way.
-struct TileModel {
-  double eff;
-  int per_cu;
-};
-TileModel tile_model(int config) {
-  switch (config) {
-    case 0: return {1.00, 1};
-    case 1: return {0.96, 1};
-    case 2: return {0.96, 1};
-    case 3: return {0.75, 2};
-    default: return {0.40, 3};
-  }
-}
-
 // Estimated time (arbitrary units) of configuration c on an m x n output: rounds of
 // co-resident tiles times the work of one round.
 double model_time(const Family& f, int c, int64_t m, int64_t n, int cus) {
   const GemmConfig* g = f.config(c);
-  const TileModel t = tile_model(c);
+  const TileModel t = f.model(c);
   const int64_t tiles = f.workgroups(c, m, n);
   const int64_t conc = std::min<int64_t>(t.per_cu, (tiles + cus - 1) / cus);
   const int64_t rounds = (tiles + cus * conc - 1) / (cus * conc);
-  return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n / t.eff;
+  return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n / (conc >= 2 ? t.eff2 : t.eff1);
 }
 
 int choose_config(const Family& f, int64_t m, int64_t n, int cus) {
