@@ -302,11 +302,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   };
 
   // The first stages' fills, before any wave has MFMA work to keep fed, come from every
-  // wave: FW per wave per stage instead of F from each filling wave.
+  // wave: FW per wave per stage instead of F from each filling wave (so the first stage
+  // boundary waits for FW-sized stages, every later one for F-sized refills).
   constexpr bool kPrologueAll = !FUSED && kFillWaves < kWaves;
   constexpr int FW = kRowGroups / kWaves;
   constexpr int FAW = (BM / RPF) / kWaves;
-  static_assert(kRowGroups % kWaves == 0 && (BM / RPF) % kWaves == 0, "prologue fills split evenly");
+  static_assert(!kPrologueAll || (kRowGroups % kWaves == 0 && (BM / RPF) % kWaves == 0),
+                "prologue fills split evenly");
   auto issue_all = [&](uint8_t* base, int k0) {
     const bool kvalid0 = k0 + 16 * fchunk0_ < K;
     const bool kvalid1 = k0 + 16 * fchunk1_ < K;
