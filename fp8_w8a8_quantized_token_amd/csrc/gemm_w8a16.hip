@@ -165,6 +165,35 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     }
   };
 
+  // The first stages' fills, before any wave has MFMA work to keep fed, come from every
+  // wave (FAA + FWA each per stage), the refills from the filling waves (F each): the
+  // first stage boundary waits for the prologue's per-wave count.
+  constexpr bool kPrologueAll = kFillWaves < kWaves;
+  constexpr int FAA = (BM / kARpf) / kWaves;
+  constexpr int FWA = (BN / kWRpf) / kWaves;
+  static_assert(!kPrologueAll || ((BM / kARpf) % kWaves == 0 && (BN / kWRpf) % kWaves == 0 && FAA >= 1 && FWA >= 1),
+                "prologue fills split evenly");
+  auto issue_all = [&](uint8_t* base, int s) {
+    const int ke0 = s * KE;
+    const bool va0 = ke0 + 8 * fac0 < K, va1 = ke0 + 8 * fac1 < K;
+#pragma unroll
+    for (int j = 0; j < FAA; ++j) {
+      const int g = wave + j * kWaves;
+      const bool odd = ((g * kARpf) & 15) != 0;
+      const uint32_t vo = (odd ? va1 : va0)
+                              ? (uint32_t)(g * kARpf) * (uint32_t)K * 2u + (odd ? faoff1 : faoff0) + (uint32_t)ke0 * 2u
+                              : kOutOfRange;
+      dma16(rsrc_a, (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024), vo);
+    }
+    const bool vw = ke0 + 16 * fwc < K;
+#pragma unroll
+    for (int j = 0; j < FWA; ++j) {
+      const int g = wave + j * kWaves;
+      const uint32_t vo = vw ? (uint32_t)(g * kWRpf) * (uint32_t)K + fwoff + (uint32_t)ke0 : kOutOfRange;
+      dma16(rsrc_w, (uint32_t)reinterpret_cast<uintptr_t>(base + kABytes + g * 1024), vo);
+    }
+  };
+
   // Operand reads of k-step h (16 k elements). Activation fragment: lane l holds row
   // l % 32, elements 8 (l / 32) .. +8 of the k-step = 16-byte chunk 2 h + l / 32.
   // Weight fragment: the same rows and elements, 8 bytes at chunk h, half l / 32.
@@ -214,12 +243,19 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   // frees stage t's buffer, which is refilled with stage t + STAGES.
   const int nst = (K + KE - 1) / KE;
   const int nsub = nst * H;
+  if constexpr (kPrologueAll) {
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nst) issue(buf(s), s);
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue_all(buf(s), s);
+    wait_stage<FAA + FWA, STAGES>(min(nst - 1, STAGES - 1));
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nst) issue(buf(s), s);
+    if (filler) wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
+    else wait_vm_lgkm0<0>();
+  }
   Frags f0, f1;
-  if (filler) wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
-  else wait_vm_lgkm0<0>();
   block_barrier();
   read_frags(buf(0), 0, f0);
 
@@ -227,7 +263,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     const int t = u / H;
     if (h == H - 1) {
       if (t + 1 < nst) {
-        if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        if (kPrologueAll && t == 0) wait_stage<FAA + FWA, STAGES>(min(nst - 2, STAGES - 2));
+        else if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
         else wait_vm_lgkm0<0>();
         block_barrier();
         if (t + STAGES < nst) issue(buf(s), t + STAGES);
