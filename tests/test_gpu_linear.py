@@ -189,6 +189,21 @@ def test_selector_is_fixed_at_construction():
         assert lin.config(m) == (cid, tm, tn, wg)  # same answer every call
 
 
+def test_selector_picks_the_measured_best_at_the_page_shapes():
+    # 256 x 256 tiles for FFN-up and the 32760-token layers, 128 x 256 for FFN-down, 64 x 64
+    # for the 26-row encoder input: the fastest configuration at each when timed on MI355X
+    dev = require_gpu()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the picks are measured for a 256-CU device")
+    up = Fp8Linear(torch.zeros((8192, 2048), dtype=torch.bfloat16, device=dev))
+    down = Fp8Linear(torch.zeros((2048, 8192), dtype=torch.bfloat16, device=dev))
+    qkv = Fp8Linear(torch.zeros((2048, 2048), dtype=torch.bfloat16, device=dev))
+    assert up.config(4096)[0] == 0
+    assert down.config(4096)[0] == 2
+    assert qkv.config(32760)[0] == 0 and down.config(32760)[0] == 0
+    assert qkv.config(26)[0] == 4
+
+
 def test_errors_are_statuses_not_crashes():
     dev = require_gpu()
     w = torch.zeros((32, 64), dtype=torch.bfloat16, device=dev)
