@@ -13,20 +13,21 @@
 //   * V_MFMA_F32_32X32X64_F8F6F4. The weight rows feed the MFMA's first operand and
 //     the activation rows its second, so a lane's results come in runs of four
 //     consecutive output channels of one token: one 8-byte bf16 store each.
-//   * Block tiles of BM tokens x BN channels, 64 bytes of k per stage, STAGES stage
-//     buffers in LDS (up to the 160 KiB of a CU). Stages are filled by
+//   * Block tiles of BM tokens x BN channels, BK = 128 bytes of k per stage, STAGES
+//     stage buffers in LDS (up to the 160 KiB of a CU). Stages are filled by
 //     buffer_load_dwordx4 ... lds (HBM/L2 -> LDS with no VGPR staging) STAGES - 1
-//     sub-steps ahead of their use, so an L2 miss has several MFMA sub-steps to land.
-//     Each wave waits with a precise vmcnt for its own fills of the stage it is about
-//     to read, then the workgroup barrier publishes every wave's fills.
+//     stages ahead of their use. Each wave waits with a precise vmcnt for its own fills
+//     of the stage it is about to read, then the workgroup barrier publishes every
+//     wave's fills.
 //   * The buffer descriptors cover only the block's valid rows, and lanes past k are
 //     pointed out of range: ragged m / n / k tails read zeros and no access leaves
 //     the operands.
-//   * LDS rows are 64 bytes; 16-byte chunk c of row r sits at position
-//     c ^ f(r), f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), which makes the fills and the
-//     ds_read_b128 operand reads free of bank conflicts.
+//   * 16-byte chunk c of LDS row r sits at position c ^ swz(r) (gemm_common.h), which
+//     makes the fills and the ds_read_b128 operand reads free of bank conflicts.
 //   * Two waves per SIMD (8-wave workgroups) for the large tiles, so one wave's
-//     barrier or LDS wait is covered by the other's MFMAs.
+//     barrier or LDS wait is covered by the other's MFMAs. A wave stalls while it issues
+//     a burst of fills, so with 8 waves only one wave per SIMD issues the refills; the
+//     first stages, before any MFMA work exists, are filled by all of them.
 //   * Workgroup ids are remapped so each of the 8 XCDs (own L2 each) walks a
 //     contiguous, m-grouped range of tiles and concurrent tiles share panels in L2.
 //   * The tile's scales and bias are requested at kernel start (one value per
