@@ -41,7 +41,8 @@
 //     traffic as a cost of the FP8 path). Per-token scales need a token's whole row
 //     before its first code and a tile needs all k of its tokens, so the first wave of
 //     workgroups quantises the tokens in shares (the per-token quantiser's arithmetic,
-//     bit for bit) and flags each share; every workgroup waits for all flags, then runs
+//     bit for bit) and flags each share; every workgroup waits for the flags of the
+//     shares holding its tile's tokens, then runs
 //     its tile as above. The weight half of the first stages is requested before the
 //     quantisation so it lands meanwhile.
 #include <algorithm>
@@ -131,22 +132,24 @@ __device__ __forceinline__ void quant_share(const GemmArgs& args, int sh, int wa
   if (threadIdx.x == 0) __hip_atomic_store(args.flags + sh, args.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until every share carries this launch's epoch. Wavefront 0 polls; a share still
-// unpublished after kStealAfterTicks is quantised here as well (identical bytes, so a
-// duplicate writer is harmless), so the wait ends even if the share's own workgroup is
-// not resident. Ends with an agent-scope acquire so the GEMM reads see every share.
+// Wait until shares [sh_begin, sh_end) (those holding this tile's tokens) carry this
+// launch's epoch. Wavefront 0 polls; a share still unpublished after kStealAfterTicks is
+// quantised here as well (identical bytes, so a duplicate writer is harmless), so the
+// wait ends even if the share's own workgroup is not resident. Ends with an agent-scope
+// acquire so the GEMM reads see the shares.
 template <int WAVES>
-__device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int lane, int* slot) {
+__device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int lane, int* slot, int sh_begin,
+                                             int sh_end) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (true) {
     if (wave == 0) {
       int missing = -1;
       while (true) {
         int first = -1;
-        for (int j0 = 0; j0 < args.shares; j0 += 64) {
+        for (int j0 = sh_begin; j0 < sh_end; j0 += 64) {
           const int j = j0 + lane;
           const bool miss =
-              j < args.shares &&
+              j < sh_end &&
               __hip_atomic_load(args.flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != args.epoch;
           const unsigned long long b = __ballot(miss);
           if (b != 0 && first < 0) first = j0 + __builtin_ctzll(b);
@@ -175,7 +178,7 @@ struct KernelTag {};
 
 // FUSED: the single-launch form. The activation codes and scales do not exist yet at
 // launch: the first `shares` workgroups quantise the bf16 activation into them
-// (quant_share), every workgroup waits for all shares (await_shares), and the weight
+// (quant_share), every workgroup waits for the shares of its tile's tokens (await_shares), and the weight
 // half of the first stages is requested before all that so it lands meanwhile.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
@@ -396,7 +399,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       if (s < nst) issue(buf(s), s * BK, 2);
     __shared__ int steal_slot;
     if (blockIdx.x < (unsigned)args.shares) quant_share<kWaves>(args, blockIdx.x, wave, lane);
-    await_shares<kWaves>(args, wave, lane, &steal_slot);
+    // only the shares holding this tile's tokens: a tile whose rows are ready starts
+    // without waiting for the slowest share elsewhere
+    const int sh_begin = m0 / args.rows_per_share;
+    const int sh_end = min(args.shares, (m0 + rows_a + args.rows_per_share - 1) / args.rows_per_share);
+    await_shares<kWaves>(args, wave, lane, &steal_slot, sh_begin, sh_end);
     if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
