@@ -117,10 +117,11 @@ TileModel w8a8_tile_model(int config) {
     default: return {0.40, 0.40, 3};
   }
 }
+// W8A16: 128 x 256 measured 4% faster than 256 x 128 at FFN-down (4096 x 2048 x 8192).
 TileModel w8a16_tile_model(int config) {
   switch (config) {
     case 0: return {1.00, 1.00, 1};
-    case 1: return {0.96, 0.96, 1};
+    case 1: return {0.95, 0.95, 1};
     case 2: return {0.96, 0.96, 1};
     case 3: return {0.75, 0.75, 2};
     default: return {0.40, 0.40, 3};
