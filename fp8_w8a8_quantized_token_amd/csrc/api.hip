@@ -75,6 +75,14 @@ int current_device_ok(int* cus = nullptr) {
   return query_device(dev, cus);
 }
 
+// A plan's weights live on the device it was created for; a run launches on the
+// current device (or the stream's, which must be the same), so the two must agree.
+int plan_device_current(int plan_device) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8W8A8_ERR_HIP;
+  return dev == plan_device ? FP8W8A8_OK : FP8W8A8_ERR_BAD_DEVICE;
+}
+
 bool valid_act(int act) {
   return act == FP8W8A8_ACT_GELU_ERF || act == FP8W8A8_ACT_GELU_TANH || act == FP8W8A8_ACT_SILU;
 }
@@ -365,6 +373,8 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
     if (workspace_bytes < fp8_linear_workspace_bytes(plan, m)) return FP8W8A8_ERR_WORKSPACE_TOO_SMALL;
   }
   if (m == 0) return FP8W8A8_OK;
+  int st = plan_device_current(plan->device);
+  if (st != FP8W8A8_OK) return st;
   const int config = plan_bucket_config(plan, m);
   if (!grid_fits(config, m, plan->n)) return FP8W8A8_ERR_BAD_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -491,6 +501,8 @@ int fp8_w8a16_run(const fp8_w8a16_plan* plan, int64_t m, const void* a_bf16, voi
   if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
   if (!aligned(a_bf16, 16) || !aligned(out_bf16, 16)) return FP8W8A8_ERR_MISALIGNED;
   if (m == 0) return FP8W8A8_OK;
+  int st = plan_device_current(plan->device);
+  if (st != FP8W8A8_OK) return st;
   const int c = bucket_config(kW8A16, plan->max_m, plan->config, plan->n, m);
   if (!grid_fits(kW8A16, c, m, plan->n)) return FP8W8A8_ERR_BAD_SHAPE;
   hipError_t e = launch_w8a16(c, plan->w_format, m, plan->n, plan->k, static_cast<const uint16_t*>(a_bf16), plan->w,

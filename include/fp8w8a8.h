@@ -190,6 +190,8 @@ size_t fp8_linear_workspace_bytes(const fp8_linear_plan* plan, int64_t m);
  * fp8_linear_run - one forward of the linear (retrospective, section 3.3: a plain
  * tensor is quantised and multiplied; an FP8 tensor goes straight to the GEMM;
  * section 3.5: an input that is already e4m3fn comes with its per-token scale).
+ * The plan's device must be the current HIP device (FP8W8A8_ERR_BAD_DEVICE
+ * otherwise, checked when m > 0), and a non-NULL stream must belong to it.
  *
  *   plan        from fp8_linear_create
  *   m           0 <= m < FP8W8A8_MAX_ROWS (0 is a no-op)
@@ -331,7 +333,8 @@ typedef struct fp8_w8a16_plan fp8_w8a16_plan;
 int fp8_w8a16_create(int device, int64_t n, int64_t k, int w_format, const void* w_fp8, const float* w_scale,
                      const void* bias_bf16, fp8_w8a16_plan** out);
 
-/* m == 0 is a no-op. a_bf16 and out_bf16 are device pointers, 16-byte aligned. */
+/* m == 0 is a no-op. a_bf16 and out_bf16 are device pointers, 16-byte aligned. As for
+ * fp8_linear_run, the plan's device must be current (else FP8W8A8_ERR_BAD_DEVICE). */
 int fp8_w8a16_run(const fp8_w8a16_plan* plan, int64_t m, const void* a_bf16, void* out_bf16, void* stream);
 
 void fp8_w8a16_destroy(fp8_w8a16_plan* plan);
