@@ -103,36 +103,43 @@ int check_weight_args(int64_t n, int64_t k, const void* w, const float* w_scale,
   return FP8W8A8_OK;
 }
 
-// Relative throughput of one workgroup of each configuration, with one workgroup on a
-// CU (eff1) and with two or more sharing it (eff2), and how many of its workgroups can
-// share a CU (LDS / register bound). The two families order their configurations the
-// same way: 256 x 256, 256 x 128, 128 x 256, 128 x 128 (4 waves), 64 x 64 (4 waves).
+// Relative k-loop throughput of one workgroup of each configuration, with one workgroup
+// on a CU (eff1) and with two or more sharing it (eff2); how many of its workgroups can
+// share a CU (LDS / register bound); and the per-tile fixed cost (prologue, epilogue,
+// output stores) in units of k, alone on a CU (f1) and shared (f2: co-resident
+// workgroups overlap one's fixed cost with the other's k loop). The two families order
+// their configurations the same way: 256 x 256, 256 x 128, 128 x 256, 128 x 128
+// (4 waves), 64 x 64 (4 waves).
 struct TileModel {
   double eff1, eff2;
   int per_cu;
+  double f1, f2;
 };
-// FP8 GEMM, measured on MI355X (the configurations interleaved in one process, 17 shapes
-// from 26 x 2048 x 2048 to 32760 x 2048 x 8192): 128 x 256 is at least as fast as
-// 256 x 128 wherever both apply (up to 11% faster at 4096 x 2048 x 2048 and
-// 1024 x 8192 x 2048), and a lone 4-wave 128 x 128 workgroup on a CU (one wave per SIMD)
-// runs at about half its rate with two sharing the CU.
+// FP8 GEMM, fitted to MI355X timings (the configurations interleaved in one process, 17
+// shapes from 26 x 2048 x 2048 to 32760 x 2048 x 8192, time per round of co-resident tiles
+// at k = 2048 and 8192): one 256 x 256 tile per CU costs the time of ~580 k of loop in fixed
+// work; the 256 x 128 and 128 x 256 tiles run their loop at ~0.84 of its rate per output
+// (128 x 256 kept ahead on ties: it was up to 11% faster at mid sizes); two co-resident
+// 4-wave 128 x 128 workgroups run at 0.75 but hide most of the fixed cost (~200 k), so they
+// win at k = 2048 and lose at k = 8192; a lone one runs at about half rate.
 TileModel w8a8_tile_model(int config) {
   switch (config) {
-    case 0: return {1.00, 1.00, 1};
-    case 1: return {0.95, 0.95, 1};
-    case 2: return {0.96, 0.96, 1};
-    case 3: return {0.45, 0.85, 2};
-    default: return {0.40, 0.40, 3};
+    case 0: return {1.00, 1.00, 1, 580, 580};
+    case 1: return {0.84, 0.84, 1, 580, 580};
+    case 2: return {0.845, 0.845, 1, 580, 580};
+    case 3: return {0.48, 0.75, 2, 580, 200};
+    default: return {0.44, 0.39, 3, 580, 240};
   }
 }
 // W8A16: 128 x 256 measured 4% faster than 256 x 128 at FFN-down (4096 x 2048 x 8192).
+// (No fixed-cost term: its picks depend on m and n only.)
 TileModel w8a16_tile_model(int config) {
   switch (config) {
-    case 0: return {1.00, 1.00, 1};
-    case 1: return {0.95, 0.95, 1};
-    case 2: return {0.96, 0.96, 1};
-    case 3: return {0.75, 0.75, 2};
-    default: return {0.40, 0.40, 3};
+    case 0: return {1.00, 1.00, 1, 0, 0};
+    case 1: return {0.95, 0.95, 1, 0, 0};
+    case 2: return {0.96, 0.96, 1, 0, 0};
+    case 3: return {0.75, 0.75, 2, 0, 0};
+    default: return {0.40, 0.40, 3, 0, 0};
   }
 }
 
@@ -153,23 +160,25 @@ bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
 }
 bool grid_fits(int config, int64_t m, int64_t n) { return grid_fits(kW8A8, config, m, n); }
 
-// Estimated time (arbitrary units) of configuration c on an m x n output: rounds of
-// co-resident tiles times the work of one round.
-double model_time(const Family& f, int c, int64_t m, int64_t n, int cus) {
+// Estimated time (arbitrary units) of configuration c on an m x n x k product: rounds of
+// co-resident tiles times the work of one round, its k loop plus its fixed cost.
+double model_time(const Family& f, int c, int64_t m, int64_t n, int64_t k, int cus) {
   const GemmConfig* g = f.config(c);
   const TileModel t = f.model(c);
   const int64_t tiles = f.workgroups(c, m, n);
   const int64_t conc = std::min<int64_t>(t.per_cu, (tiles + cus - 1) / cus);
   const int64_t rounds = (tiles + cus * conc - 1) / (cus * conc);
-  return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n / (conc >= 2 ? t.eff2 : t.eff1);
+  const bool shared = conc >= 2;
+  return (double)rounds * conc * (double)g->tile_m * (double)g->tile_n * ((double)k + (shared ? t.f2 : t.f1)) /
+         (shared ? t.eff2 : t.eff1);
 }
 
-int choose_config(const Family& f, int64_t m, int64_t n, int cus) {
+int choose_config(const Family& f, int64_t m, int64_t n, int64_t k, int cus) {
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < f.count(); ++c) {
     if (!grid_fits(f, c, m, n)) continue;
-    const double t = model_time(f, c, m, n, cus);
+    const double t = model_time(f, c, m, n, k, cus);
     if (best < 0 || t < best_t) {
       best = c;
       best_t = t;
@@ -183,11 +192,11 @@ int choose_config(const Family& f, int64_t m, int64_t n, int cus) {
 constexpr int kBuckets = 6;
 constexpr int64_t kBucketBounds[kBuckets] = {64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
 
-void fill_buckets(const Family& f, int64_t n, int cus, int64_t* max_m, int* config) {
+void fill_buckets(const Family& f, int64_t n, int64_t k, int cus, int64_t* max_m, int* config) {
   for (int b = 0; b < kBuckets; ++b) {
     max_m[b] = kBucketBounds[b];
     const int64_t rep = b + 1 < kBuckets ? kBucketBounds[b] : 32768;
-    config[b] = choose_config(f, rep, n, cus);
+    config[b] = choose_config(f, rep, n, k, cus);
   }
 }
 
@@ -344,7 +353,7 @@ int fp8_linear_create(int device, int64_t n, int64_t k, const void* w_fp8, const
   p->w_scale = w_scale;
   p->bias = static_cast<const uint16_t*>(bias_bf16);
   p->cu_count = cus > 0 ? cus : 256;
-  fill_buckets(kW8A8, n, p->cu_count, p->max_m, p->config);
+  fill_buckets(kW8A8, n, k, p->cu_count, p->max_m, p->config);
   *out = p;
   return FP8W8A8_OK;
 }
@@ -491,7 +500,7 @@ int fp8_w8a16_create(int device, int64_t n, int64_t k, int w_format, const void*
   p->w_scale = w_scale;
   p->bias = static_cast<const uint16_t*>(bias_bf16);
   p->cu_count = cus > 0 ? cus : 256;
-  fill_buckets(kW8A16, n, p->cu_count, p->max_m, p->config);
+  fill_buckets(kW8A16, n, k, p->cu_count, p->max_m, p->config);
   *out = p;
   return FP8W8A8_OK;
 }

@@ -18,6 +18,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer descriptor, word 3
+constexpr int kCpolNt = 2;                 // cache-policy operand of buffer stores: nt
 
 
 // Raw buffer descriptor in SGPRs: 48-bit base, stride 0, num_records bytes.
@@ -57,7 +58,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // m x n row-major bf16 matrix. Each store writes 64 / RC whole rows of the wave tile, 16
 // bytes per lane. The buffer descriptor covers exactly the tile's valid rows, so rows
 // past m fall outside it and are dropped, and lanes whose 8 columns lie past n are
-// pointed out of range: no per-store bounds test.
+// pointed out of range: no per-store bounds test. The stores are non-temporal: the output
+// is not read again by this kernel, and marking its lines for early eviction keeps the
+// operand panels other tiles still read in the XCD's L2 (FFN-up 68.5 -> 66.1 us,
+// 32760 x 2048 x 2048 138.3 -> 129.5 us, bit-identical output).
 template <int WTM, int RC>
 __device__ __forceinline__ void store_wave_tile(const uint8_t* wout, int lane, uint16_t* out, int m, int n,
                                                 int row0, int col0) {
@@ -76,7 +80,8 @@ __device__ __forceinline__ void store_wave_tile(const uint8_t* wout, int lane, u
     const int r = t * kRowsPerStore + lane / RC;
     const uint4 v = *reinterpret_cast<const uint4*>(wout + r * (RC * 16) + ((c ^ (r % RC)) << 4));
     const v4u data = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(data, rsrc, voff + (uint32_t)(t * kRowsPerStore) * row_bytes, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(data, rsrc, voff + (uint32_t)(t * kRowsPerStore) * row_bytes, 0,
+                                           kCpolNt);
   }
 }
 

@@ -106,10 +106,14 @@ __device__ __forceinline__ void load_row(const uint16_t* xr, int nchunks, int la
 // How a row's results reach memory: plain stores (the default), or a policy with the
 // same two members (the single-launch quantise + GEMM kernel writes through to the
 // device coherence point). `qr` is the row's code pointer (uniform across the
-// wavefront), `c` a 16-code chunk index.
+// wavefront), `c` a 16-code chunk index. The codes are stored non-temporal: the next
+// reader is another kernel, mostly on other XCDs, so they need not stay in this XCD's
+// L2 (FFN-up quantise + GEMM 65.9 -> 65.1 us).
 struct PlainStore {
+  typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
   __device__ __forceinline__ void codes(uint8_t* qr, int c, int, const uint4& v) const {
-    *reinterpret_cast<uint4*>(qr + static_cast<int64_t>(c) * 16) = v;
+    __builtin_nontemporal_store((v4u32){v.x, v.y, v.z, v.w},
+                                reinterpret_cast<v4u32*>(qr + static_cast<int64_t>(c) * 16));
   }
   __device__ __forceinline__ void scale(float* srow, float s) const { *srow = s; }
 };

@@ -158,7 +158,7 @@ int fp8_act_quant_rows(const void* x_bf16, int64_t rows, int64_t cols, const voi
 /*
  * A constructed linear: validated shapes, borrowed weight pointers and the GEMM
  * kernel configuration chosen for each activation-row bucket. The choice is made
- * once here from (n, k, bias present, compute-unit count), as the retrospective's
+ * once here from (n, k, compute-unit count), as the retrospective's
  * section 3.3 asks (bind the backend at construction, keep the forward narrow),
  * and per call only one integer compare on m picks the bucket (section 3.2: FFN-up
  * and FFN-down shapes want different tiles).
