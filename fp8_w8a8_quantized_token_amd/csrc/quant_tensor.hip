@@ -27,6 +27,7 @@ namespace fp8w8a8 {
 namespace {
 
 constexpr int kBlock = 256;
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 constexpr int kMaxPartials = 1024;
 
 __device__ __forceinline__ uint32_t pack4_bf8(float a, float b, float c, float d) {
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
       else
         o = qrow::quant16<qrow::Mode::kExact>(a, b, s, r);
     }
-    q[i] = o;
+    // non-temporal: the codes are not read again here (8192 x 2048: 19.1 -> 18.2 us)
+    __builtin_nontemporal_store((v4u32){o.x, o.y, o.z, o.w}, reinterpret_cast<v4u32*>(q + i));
   }
 }
 
