@@ -143,3 +143,18 @@ def test_ffn_full_size_sampled_rows(name):
     rows = sample_rows(a.shape[0])
     ref = ow.w8a16_ref(bf16_bits(a)[rows], qw, sw, bf16_bits(b))
     assert_linear_close(out[rows], ref, f"w8a16 {name} sampled rows")
+
+
+@pytest.mark.gpu
+def test_w8a16_selector_picks_the_measured_best():
+    # timed on MI355X (every configuration interleaved in one process): 256 x 256 at FFN-up,
+    # 128 x 256 at FFN-down, 128 x 128 at 512 x 8192 x 2048 and 2048 x 2048 x 8192, 64 x 64 for
+    # 26 and 256 rows
+    dev = require_gpu()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the picks are measured for a 256-CU device")
+    up = fp8.Fp8WeightOnlyLinear(torch.zeros((8192, 2048), dtype=torch.bfloat16, device=dev))
+    down = fp8.Fp8WeightOnlyLinear(torch.zeros((2048, 8192), dtype=torch.bfloat16, device=dev))
+    assert up.config(4096)[0] == 0 and down.config(4096)[0] == 2
+    assert up.config(512)[0] == 3 and down.config(2048)[0] == 3
+    assert up.config(256)[0] == 4 and down.config(26)[0] == 4
