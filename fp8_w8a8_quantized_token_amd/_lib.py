@@ -18,6 +18,7 @@ ERR_MISALIGNED = -3
 ERR_BAD_DEVICE = -4
 ERR_WORKSPACE_TOO_SMALL = -5
 ERR_HIP = -6
+ERR_CAPTURE = -7
 
 A_BF16 = 0
 A_E4M3 = 1

@@ -247,6 +247,7 @@ const char* fp8w8a8_status_string(int status) {
     case FP8W8A8_ERR_BAD_DEVICE: return "bad device: not a gfx950 (MI355X-class) GPU";
     case FP8W8A8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small: see fp8_linear_workspace_bytes";
     case FP8W8A8_ERR_HIP: return "HIP runtime error";
+    case FP8W8A8_ERR_CAPTURE: return "not capturable: this call cannot be recorded into a HIP graph";
     default: return "unknown status";
   }
 }
@@ -483,6 +484,11 @@ int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const vo
   int cus = 0;
   st = current_device_ok(&cus);
   if (st != FP8W8A8_OK) return st;
+  // The launch's generation number is a kernel argument chosen here: a captured graph
+  // would replay it, and its flags from the previous replay would already match.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capture) != hipSuccess) return FP8W8A8_ERR_HIP;
+  if (capture != hipStreamCaptureStatusNone) return FP8W8A8_ERR_CAPTURE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* ws_scale = reinterpret_cast<float*>(ws + align256((size_t)m * (size_t)k));
   auto* flags = reinterpret_cast<unsigned long long*>(reinterpret_cast<uint8_t*>(ws_scale) +

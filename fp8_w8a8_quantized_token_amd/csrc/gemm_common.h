@@ -35,11 +35,14 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 // buffer_load_dwordx4 ... lds: lane i's 16 bytes land at LDS address lds + 16 i. Issued
 // from inline asm so the compiler does not make every later LDS read wait for all
 // fills in flight; the kernel waits for exactly the fills it needs (vmcnt) and
-// synchronises the workgroup itself. The instruction has no register result.
+// synchronises the workgroup itself. The instruction has no register result. The LDS
+// address goes in through M0 as an operand bound to that register ("{m0}"), so the
+// compiler writes M0 itself and knows its contents, rather than having it changed
+// behind its back inside the asm.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
                : "memory");
 }
 

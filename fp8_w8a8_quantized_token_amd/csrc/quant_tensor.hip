@@ -17,9 +17,13 @@
 // quotients reuse the per-token quantiser's arithmetic (quant_row.h, including its
 // divide-free fast path); e5m2 quotients take an IEEE division, since its subnormal
 // range reaches quotients below the fast path's proven range. v_cvt_pk_bf8_f32 /
-// v_cvt_pk_fp8_f32 round to nearest even into the OCP encodings; quotients never
-// exceed fmax * (1 + 2^-23), which both round to fmax. Dequantisation converts codes
-// exactly with v_cvt_pk_f32_{fp8,bf8} and multiplies once in fp32.
+// v_cvt_pk_fp8_f32 round to nearest even into the OCP encodings and do not saturate.
+// e4m3fn quotients stay below 464 (the midpoint above 448) for every bf16 pair
+// (x, amax), fp32-subnormal scales included. e5m2 quotients do not: for a bf16 amax of
+// 1..3 x 2^-133 the scale fl32(amax / 57344) is an fp32 subnormal of 1..3 units that
+// rounded down, and amax / s = 65536 would convert to infinity; they are clamped to
+// +-57344 first (which keeps the sign of -0). Dequantisation converts codes exactly
+// with v_cvt_pk_f32_{fp8,bf8} and multiplies once in fp32.
 #include "internal.h"
 #include "quant_row.h"
 
@@ -36,6 +40,9 @@ __device__ __forceinline__ uint32_t pack4_bf8(float a, float b, float c, float d
   return static_cast<uint32_t>(w);
 }
 
+// Clamp a quotient to the largest finite e5m2 magnitude (57344), sign kept.
+__device__ __forceinline__ float sat_e5m2(float q) { return fminf(fmaxf(q, -57344.0f), 57344.0f); }
+
 // 16 bf16 (two uint4) -> 16 e5m2 codes: IEEE quotient (or the value itself when s == 0)
 __device__ __forceinline__ uint4 quant16_e5m2(const uint4& a, const uint4& b, float s, bool zero) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -44,7 +51,8 @@ __device__ __forceinline__ uint4 quant16_e5m2(const uint4& a, const uint4& b, fl
   for (int i = 0; i < 4; ++i) {
     const uint32_t u0 = w[2 * i], u1 = w[2 * i + 1];
     const float x0 = qrow::bf16_lo(u0), x1 = qrow::bf16_hi(u0), x2 = qrow::bf16_lo(u1), x3 = qrow::bf16_hi(u1);
-    o[i] = zero ? pack4_bf8(x0, x1, x2, x3) : pack4_bf8(x0 / s, x1 / s, x2 / s, x3 / s);
+    o[i] = zero ? pack4_bf8(x0, x1, x2, x3) : pack4_bf8(sat_e5m2(x0 / s), sat_e5m2(x1 / s), sat_e5m2(x2 / s),
+                                                         sat_e5m2(x3 / s));
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }

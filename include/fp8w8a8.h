@@ -60,6 +60,7 @@ extern "C" {
 #define FP8W8A8_ERR_BAD_DEVICE (-4)           /* the device is not a gfx950 GPU */
 #define FP8W8A8_ERR_WORKSPACE_TOO_SMALL (-5)  /* the workspace is smaller than fp8_linear_workspace_bytes */
 #define FP8W8A8_ERR_HIP (-6)                  /* a HIP runtime call or launch failed */
+#define FP8W8A8_ERR_CAPTURE (-7)              /* the call cannot be recorded into a HIP graph (fp8_quant_gemm) */
 
 /* ---- activation kinds for fp8_linear_run ------------------------------------ */
 #define FP8W8A8_A_BF16 0  /* a is bf16 [m, k]; the run quantises it per token into the workspace */
@@ -254,12 +255,19 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
  * per-token quantisation (bit-identical to fp8_quant_rows) and the GEMM with its
  * epilogue (bit-identical to fp8_gemm_run_config's configuration 0, 256 x 256 tiles)
  * in ONE kernel launch: the first wave of workgroups quantises the tokens in shares
- * into the workspace and publishes a flag per share; every workgroup waits until all
- * shares are published (quantising itself any share whose owner has not published
- * within 100 us, so the wait ends even when not all workgroups are resident), then
- * runs its output tile on the codes. Same result as fp8_quant_rows followed by the
- * GEMM; on MI355X it is no faster than those two launches (see the bench's
- * quant_gemm record), so fp8_linear_run keeps the two launches.
+ * into the workspace and publishes a flag per share; every workgroup waits until the
+ * shares that hold its own tile's tokens are published (quantising itself any such
+ * share whose owner has not published within 100 us, so the wait ends even when not
+ * all workgroups are resident), then runs its output tile on the codes. Same result
+ * as fp8_quant_rows followed by the GEMM; on MI355X it is no faster than those two
+ * launches (see the bench's quant_gemm record), so fp8_linear_run keeps the two
+ * launches.
+ *
+ * A flag holds the launch's generation number, which the host picks per call and
+ * passes to the kernel. A HIP graph would replay the recorded number, and from the
+ * second replay on every flag would already match before its share is rewritten, so
+ * a call on a stream that is being captured is refused with FP8W8A8_ERR_CAPTURE
+ * (nothing is launched or recorded).
  *
  *   m, n, k    as fp8_linear_create / fp8_linear_run (0 <= m < FP8W8A8_MAX_ROWS)
  *   a_bf16     device, bf16 [m, k], 16-byte aligned
@@ -270,7 +278,7 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
  *              then the launch flags. After the call the codes and scales hold the
  *              quantised activation. Prior contents do not matter (no clearing needed);
  *              two calls that overlap in time must not share a workspace.
- *   stream     hipStream_t or NULL; one launch, no synchronisation
+ *   stream     hipStream_t or NULL, not under graph capture; one launch, no synchronisation
  */
 size_t fp8_quant_gemm_workspace_bytes(int64_t m, int64_t k);
 int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const void* w_fp8,

@@ -23,11 +23,8 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
-def decode(codes):
-    """Real value of each e4m3fn byte, as float64 (NaN for 0x7F / 0xFF, -0.0 for 0x80)."""
-    c = np.asarray(codes).astype(np.int64)
-    if c.size and (c.min() < 0 or c.max() > 255):
-        raise ValueError("e4m3fn codes are bytes 0..255")
+def _decode_formula(c):
+    """The closed form above, evaluated elementwise on int64 codes 0..255."""
     sign = (c >> 7) & 1
     exp = (c >> 3) & 0xF
     man = c & 0x7
@@ -37,6 +34,21 @@ def decode(codes):
     mag = np.where(exp == 0, sub, norm)
     mag = np.where((exp == 15) & (man == 7), np.nan, mag)
     return np.where(sign == 1, -mag, mag)
+
+
+# The closed form evaluated once on all 256 codes; decode() looks values up here, so
+# decoding a large matrix costs one indexing pass rather than the formula per element.
+_VALUES = _decode_formula(np.arange(256, dtype=np.int64))
+
+
+def decode(codes):
+    """Real value of each e4m3fn byte, as float64 (NaN for 0x7F / 0xFF, -0.0 for 0x80)."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        c = c.astype(np.int64)
+        if c.size and (c.min() < 0 or c.max() > 255):
+            raise ValueError("e4m3fn codes are bytes 0..255")
+    return _VALUES[c]
 
 
 def encode(values):

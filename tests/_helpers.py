@@ -40,11 +40,34 @@ def assert_linear_close(gpu_out, ref, label=""):
     return elem, fro
 
 
-def sample_rows(m, tile=256, count=192, seed=0):
-    """Rows to check at full size: the first tile's rows, the ragged last tile, and random ones."""
-    rng = np.random.default_rng(seed)
-    head = np.arange(min(m, 32))
-    last_tile = (m - 1) // tile * tile
-    tail = np.arange(max(0, min(last_tile, m - 48)), m)
-    rand = rng.choice(m, size=min(m, count), replace=False)
-    return np.unique(np.concatenate([head, tail, rand]))
+def assert_linear_close_rows(out_gpu, ref_rows, label="", chunk=4096):
+    """Whole-output parity of a GPU output [m, n] against the oracle, row block by row block.
+
+    ref_rows(r0, r1) returns the oracle's unrounded float64 rows [r0, r1). Every element
+    must meet the elementwise bound, and the relative Frobenius error is accumulated over
+    the whole [m, n] output (not per block)."""
+    m = out_gpu.shape[0]
+    worst, num, den = 0.0, 0.0, 0.0
+    for r0 in range(0, m, chunk):
+        r1 = min(m, r0 + chunk)
+        ref = ref_rows(r0, r1)
+        got = bf16_out_to_f64(out_gpu[r0:r1])
+        assert got.shape == ref.shape, (got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), f"{label}: non-finite output in rows {r0}..{r1}"
+        diff = got - ref
+        worst = max(worst, float(np.max(np.abs(diff) / (np.abs(ref) + 1.0))) if ref.size else 0.0)
+        num += float(np.sum(diff * diff))
+        den += float(np.sum(ref * ref))
+    fro = float(np.sqrt(num) / np.sqrt(den)) if den > 0 else float(np.sqrt(num))
+    assert worst <= ELEM_TOL, f"{label}: max |gpu-ref|/(|ref|+1) = {worst:.3e} > {ELEM_TOL}"
+    assert fro <= FRO_TOL, f"{label}: relative Frobenius error {fro:.3e} > {FRO_TOL} over the whole output"
+    return worst, fro
+
+
+def assert_codes_equal(q_gpu, s_gpu, eq, es, label=""):
+    """Bit-exact comparison of per-row codes [m, k] and scales [m] with the oracle's."""
+    q = q_gpu.cpu().numpy() if isinstance(q_gpu, torch.Tensor) else q_gpu
+    s = s_gpu.cpu().numpy() if isinstance(s_gpu, torch.Tensor) else s_gpu
+    assert np.array_equal(s.view(np.uint32), np.asarray(es, np.float32).view(np.uint32)), f"{label}: scales differ"
+    bad = np.argwhere(q != eq)
+    assert bad.size == 0, f"{label}: {len(bad)} codes differ, first at {bad[0]}"

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import fp8_w8a8_quantized_token_amd as fp8
-from oracle import act as oact, linear as ol, quant as oq
-from tests._helpers import assert_linear_close, require_gpu, sample_rows
+from oracle import act as oact, cref, linear as ol, quant as oq
+from tests._helpers import assert_codes_equal, assert_linear_close, require_gpu
 from workloads import bf16_bits, make_case
 
 pytestmark = pytest.mark.gpu
@@ -118,15 +118,16 @@ def test_fused_equals_unfused_on_gpu(dev, tables, kind, rows, cols):
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
-def test_fused_producer_full_size_ffn_down_input(dev, tables):
-    # the FFN-down input at the FFN shapes: [4096, 8192], checked on sampled rows
-    x = _normal(4096, 8192, seed=21)
+@pytest.mark.parametrize("rows", [4096, 32760])
+def test_fused_producer_full_size_ffn_down_input(dev, tables, rows):
+    # the FFN-down input at the FFN shape [4096, 8192] and at the DiT-block size [32760, 8192],
+    # every row: the oracle's exact activation table, then the C statement of the per-token
+    # quantiser (pinned bit for bit to oracle.quant)
+    x = _normal(rows, 8192, seed=21)
     q, s = fp8.act_quant_rows(x.to(dev), tables["gelu_tanh"])
-    q, s = q.cpu().numpy(), s.cpu().numpy()
-    rows = sample_rows(4096, tile=16, count=96, seed=1)
-    eq, es = oact.act_quant_rows(bf16_bits(x)[rows], "gelu_tanh")
-    assert np.array_equal(q[rows], eq)
-    assert np.array_equal(s[rows].view(np.uint32), es.view(np.uint32))
+    torch.cuda.synchronize()
+    eq, es = cref.quant_rows(oact.act_bf16_bits(bf16_bits(x), "gelu_tanh"))
+    assert_codes_equal(q, s, eq, es, f"gelu_tanh producer [{rows}, 8192]")
 
 
 def test_fused_producer_feeds_the_fp8_linear(dev, tables):

@@ -5,8 +5,10 @@ the same bf16 inputs (the oracle quantises them itself): elementwise
 |gpu - ref| <= 1e-2 (|ref| + 1) and relative Frobenius error <= 2e-3. Quantised
 activations and weights are compared bit for bit on the way. Covered: the tiny
 config in full; every compiled GEMM configuration on ragged m / n / k tails; the
-selector's plans at the four full-size workloads on sampled rows; the e4m3fn
-pass-through input; A = 0 (output == bias exactly); no bias; guard bands.
+selector's plans at the four full-size workloads, every output element against the
+oracle (elementwise bound on each, relative Frobenius error over the whole output) and
+every activation code and scale bit for bit; the e4m3fn pass-through input on the
+oracle's own codes; A = 0 (output == bias exactly); no bias; guard bands.
 """
 
 import ctypes
@@ -17,8 +19,8 @@ import torch
 
 import fp8_w8a8_quantized_token_amd as fp8
 from fp8_w8a8_quantized_token_amd import Fp8Linear, gemm_config_count, gemm_run_config, quant_rows
-from oracle import e4m3, linear as ol, quant as oq
-from tests._helpers import assert_linear_close, bf16_out_to_f64, require_gpu, sample_rows
+from oracle import cref, linear as ol, quant as oq
+from tests._helpers import assert_codes_equal, assert_linear_close, assert_linear_close_rows, require_gpu
 from workloads import bf16_bits, make_case, make_config
 
 pytestmark = pytest.mark.gpu
@@ -93,16 +95,25 @@ def test_no_bias_and_gelu_input():
 
 
 def test_fp8_input_passthrough_matches_bf16_path():
+    # an input that is already e4m3fn goes straight to the GEMM with the scales passed in;
+    # the codes here are the oracle's own (not the GPU quantiser's), so the check of the
+    # pass-through against the oracle depends on no other GPU step
     dev = require_gpu()
     case = make_case(333, 384, 1024, seed=6)
     lin = Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    eqa, esa = oq.quant_rows(bf16_bits(case.a))
+    qw, sw = _oracle_weight(case.w)
+    ref = ol.linear_ref_fp8(eqa, esa, qw, sw, bf16_bits(case.bias))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    out_fp8 = lin(t(eqa).view(torch.float8_e4m3fn), t(esa))
+    out_u8 = lin(t(eqa), t(esa))
     a = case.a.to(dev)
     out_bf16 = lin(a)
-    qa, sa = quant_rows(a)
-    out_fp8 = lin(qa.view(torch.float8_e4m3fn), sa)
-    out_u8 = lin(qa, sa)
     torch.cuda.synchronize()
-    assert torch.equal(out_bf16, out_fp8) and torch.equal(out_bf16, out_u8)
+    assert_linear_close(out_fp8, ref, "e4m3fn pass-through")
+    assert torch.equal(out_fp8, out_u8)
+    # the bf16 input quantises to the same codes, so the two forwards agree bit for bit
+    assert torch.equal(out_bf16, out_fp8)
 
 
 def test_three_dim_input_and_out_buffer_guard_band():
@@ -123,22 +134,34 @@ def test_three_dim_input_and_out_buffer_guard_band():
     assert_linear_close(out.reshape(m, n), ref, "3-d input")
 
 
-def _full_size_linear(a_cpu, w_cpu, b_cpu, dev, label, rows=None, qa_gpu=None, sa_gpu=None, lin=None):
-    """Run the plan at full size on the GPU, check sampled rows against the oracle."""
+def _full_size_linear(a_cpu, w_cpu, b_cpu, dev, label, qa_gpu=None, sa_gpu=None, lin=None, oracle_codes=None,
+                      oracle_weight=None):
+    """Run the plan at full size on the GPU and compare its whole output with the oracle.
+
+    The oracle's codes come from the C statement of the per-token quantiser (pinned bit
+    for bit to oracle.quant). A bf16 run leaves its codes and scales in the workspace;
+    those are compared bit for bit too. An e4m3fn run (qa_gpu, sa_gpu) takes the codes
+    the caller produced and checked."""
     if lin is None:
         lin = Fp8Linear(w_cpu.to(dev), b_cpu.to(dev))
+    m, k = a_cpu.shape
+    eqa, esa = oracle_codes if oracle_codes is not None else cref.quant_rows(bf16_bits(a_cpu))
+    qw, sw = oracle_weight if oracle_weight is not None else cref.quant_rows(bf16_bits(w_cpu))
     if qa_gpu is None:
-        out = lin(a_cpu.to(dev))
+        ws = torch.empty((lin.workspace_bytes(m),), dtype=torch.uint8, device=dev)
+        out = lin(a_cpu.to(dev), workspace=ws)
+        torch.cuda.synchronize()
+        codes_bytes = (m * k + 255) // 256 * 256
+        assert_codes_equal(ws[: m * k].view(m, k), ws[codes_bytes: codes_bytes + 4 * m].view(torch.float32),
+                           eqa, esa, f"{label} activation")
     else:
         out = lin(qa_gpu, sa_gpu)
-    torch.cuda.synchronize()
-    m = a_cpu.shape[0]
-    rows = sample_rows(m) if rows is None else rows
-    qw, sw = _oracle_weight(w_cpu)
+        torch.cuda.synchronize()
     assert np.array_equal(lin.w_fp8.cpu().numpy(), qw), f"{label}: weight codes differ"
-    ref, _, _ = ol.linear_ref(bf16_bits(a_cpu)[rows], qw, sw, bf16_bits(b_cpu))
-    got = bf16_out_to_f64(out[torch.from_numpy(rows).to(dev)])
-    return assert_linear_close(got, ref, label)
+    assert np.array_equal(lin.w_scale.cpu().numpy().view(np.uint32), sw.view(np.uint32)), f"{label}: weight scales"
+    bias_bits = _bias_bits(b_cpu)
+    return assert_linear_close_rows(
+        out, lambda r0, r1: ol.linear_ref_fp8(eqa[r0:r1], esa[r0:r1], qw, sw, bias_bits), label)
 
 
 @pytest.mark.slow
@@ -157,25 +180,49 @@ def test_qkv_shared_quantisation_full_size():
     hidden, enc = cfg["activations"]["hidden"], cfg["activations"]["encoder"]
     qh, sh = quant_rows(hidden.to(dev))  # quantised once, fed to all three projections
     qe, se = quant_rows(enc.to(dev))
+    torch.cuda.synchronize()
+    codes_h = cref.quant_rows(bf16_bits(hidden))
+    codes_e = cref.quant_rows(bf16_bits(enc))
+    assert_codes_equal(qh, sh, *codes_h, "qkv/hidden")
+    assert_codes_equal(qe, se, *codes_e, "qkv/encoder")
     for layer in ("q", "k", "v"):
         w, b = cfg["weights"][layer], cfg["biases"][layer]
         lin = Fp8Linear(w.to(dev), b.to(dev))
-        _full_size_linear(hidden, w, b, dev, f"qkv/{layer}", qa_gpu=qh, sa_gpu=sh, lin=lin)
-        _full_size_linear(enc, w, b, dev, f"qkv/{layer}_enc", rows=np.arange(26), qa_gpu=qe, sa_gpu=se, lin=lin)
+        wq = cref.quant_rows(bf16_bits(w))
+        _full_size_linear(hidden, w, b, dev, f"qkv/{layer}", qa_gpu=qh, sa_gpu=sh, lin=lin, oracle_codes=codes_h,
+                          oracle_weight=wq)
+        _full_size_linear(enc, w, b, dev, f"qkv/{layer}_enc", qa_gpu=qe, sa_gpu=se, lin=lin, oracle_codes=codes_e,
+                          oracle_weight=wq)
+        # the same plan on the bf16 input quantises it itself, bit for bit the same codes
+        _full_size_linear(enc, w, b, dev, f"qkv/{layer}_enc bf16 input", lin=lin, oracle_codes=codes_e,
+                          oracle_weight=wq)
+
+
+@pytest.fixture(scope="module")
+def dit_block():
+    """The DiT-block config, each activation quantised once on the GPU (codes checked
+    against the oracle by the tests that use them) and by the oracle."""
+    dev = require_gpu()
+    cfg = make_config("dit_block")
+    gpu, oracle = {}, {}
+    for name, a in cfg["activations"].items():
+        gpu[name] = quant_rows(a.to(dev))
+        oracle[name] = cref.quant_rows(bf16_bits(a))
+    torch.cuda.synchronize()
+    return cfg, gpu, oracle
 
 
 @pytest.mark.slow
-def test_dit_block_full_size():
+@pytest.mark.parametrize("layer", ["q", "k", "v", "out", "ffn_up", "ffn_down"])
+def test_dit_block_full_size(dit_block, layer):
     dev = require_gpu()
-    cfg = make_config("dit_block")
-    quantised = {}
-    for name, a in cfg["activations"].items():
-        quantised[name] = quant_rows(a.to(dev))
-    for layer, act in cfg["layers"]:
-        w, b = cfg["weights"][layer], cfg["biases"][layer]
-        qa, sa = quantised[act]
-        _full_size_linear(cfg["activations"][act], w, b, dev, f"dit/{layer}", qa_gpu=qa, sa_gpu=sa,
-                          rows=sample_rows(cfg["activations"][act].shape[0], count=96))
+    cfg, gpu, oracle = dit_block
+    act = dict(cfg["layers"])[layer]
+    qa, sa = gpu[act]
+    assert_codes_equal(qa, sa, *oracle[act], f"dit/{act}")
+    w, b = cfg["weights"][layer], cfg["biases"][layer]
+    _full_size_linear(cfg["activations"][act], w, b, dev, f"dit/{layer}", qa_gpu=qa, sa_gpu=sa,
+                      oracle_codes=oracle[act])
 
 
 def test_selector_is_fixed_at_construction():

@@ -6,7 +6,8 @@ random tensors of several sizes (one 16-element group, ragged grid-stride tails,
 weight-sized tensor) in both formats; every finite bf16 value through each format's
 conversion (a tensor whose amax equals the format's largest value has scale 1, so
 the quotients are the values themselves); zero tensors; tensors whose scale is an
-fp32 subnormal (the exact-division path); the dequantisation of every code.
+fp32 subnormal (the exact-division path), down to the smallest bf16 amax values, whose
+e5m2 quotients overflow the format and must saturate; the dequantisation of every code.
 """
 
 import numpy as np
@@ -72,6 +73,21 @@ def test_zero_and_subnormal_scale_tensors(fmt):
     rng = np.random.default_rng(7)
     tiny = rng.integers(1, 0x0400, 256).astype(np.uint16) | (rng.integers(0, 2, 256).astype(np.uint16) << 15)
     _check(tiny, fmt, dev)  # amax < 2^-120: the scale is an fp32 subnormal
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("amax_bits", range(1, 8))
+def test_smallest_subnormal_amax(fmt, amax_bits):
+    # amax = amax_bits x 2^-133 (a bf16 subnormal): the scale has only a few significant
+    # bits, and for e5m2 with amax_bits <= 3 it rounds down so far that amax / s = 65536
+    # lies above the format's largest value and must saturate to 57344 (0x7B).
+    dev = require_gpu()
+    rng = np.random.default_rng(amax_bits)
+    body = rng.integers(0, amax_bits + 1, 96).astype(np.uint16)
+    body |= rng.integers(0, 2, 96).astype(np.uint16) << 15
+    body[5] = amax_bits
+    body[17] = amax_bits | 0x8000
+    _check(body, fmt, dev)
 
 
 @pytest.mark.parametrize("fmt", FMTS)

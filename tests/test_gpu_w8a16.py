@@ -17,7 +17,7 @@ import torch
 
 import fp8_w8a8_quantized_token_amd as fp8
 from oracle import e4m3, e5m2, quant as oq, tensor_quant as otq, w8a16 as ow
-from tests._helpers import assert_linear_close, require_gpu, sample_rows
+from tests._helpers import assert_linear_close, assert_linear_close_rows, require_gpu
 from workloads import bf16_bits, make_case, make_config
 
 pytestmark = pytest.mark.gpu
@@ -131,18 +131,18 @@ def test_per_tensor_weights_from_the_state_dict_converter(fmt):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["ffn_up", "ffn_down"])
-def test_ffn_full_size_sampled_rows(name):
+def test_ffn_full_size(name):
     dev = require_gpu()
     cfg = make_config(name)
     a = cfg["activations"]["a"]
     w, b = cfg["weights"][name], cfg["biases"][name]
     lin = fp8.Fp8WeightOnlyLinear(w.to(dev), b.to(dev))
-    out = lin(a.to(dev)).cpu()
+    out = lin(a.to(dev))
+    torch.cuda.synchronize()
     qw, sw = oq.quant_weights_per_channel(bf16_bits(w))
     assert np.array_equal(lin.w_fp8.cpu().numpy(), qw)
-    rows = sample_rows(a.shape[0])
-    ref = ow.w8a16_ref(bf16_bits(a)[rows], qw, sw, bf16_bits(b))
-    assert_linear_close(out[rows], ref, f"w8a16 {name} sampled rows")
+    a_bits, b_bits = bf16_bits(a), bf16_bits(b)
+    assert_linear_close_rows(out, lambda r0, r1: ow.w8a16_ref(a_bits[r0:r1], qw, sw, b_bits), f"w8a16 {name}")
 
 
 @pytest.mark.gpu

@@ -51,6 +51,23 @@ def test_hand_codes_e5m2():
     assert q.tolist() == [0x7B, 0xE6, 0x5C, 0x6A]
 
 
+def test_worked_subnormal_scale_saturates_e5m2():
+    # amax = 2^-133, the smallest positive bf16 (bits 0x0001). amax / 57344 = (8/7) * 2^-149
+    # lies between the fp32 subnormals 2^-149 and 2^-148, nearer the first: s = 2^-149.
+    # The quotient amax / s = 2^16 = 65536 is above 57344 and saturates to 0x7B (0xFB for
+    # -amax); half of amax gives 2^15 = 32768 = 1.0 * 2^15 -> E = 30, M = 0 -> 0x78.
+    bits = np.array([0x0001, 0x8001, 0x0000, 0x8000], np.uint16)
+    q, s = tq.quant_tensor(bits, "e5m2")
+    assert np.float32(s).view(np.uint32) == 1  # 2^-149
+    assert q.tolist() == [0x7B, 0xFB, 0x00, 0x80]
+    assert e5m2.decode(np.array([0x78], np.uint8))[0] == 32768.0
+    # e4m3fn: amax / 448 = (2^16 / 448) * 2^-149 = 146.29 units of 2^-149 -> s = 146 * 2^-149,
+    # quotient 65536 / 146 = 448.88 (below the 464 midpoint), saturating to 448 (0x7E)
+    q4, s4 = tq.quant_tensor(bits, "e4m3fn")
+    assert np.float32(s4).view(np.uint32) == 146
+    assert q4.tolist() == [0x7E, 0xFE, 0x00, 0x80]
+
+
 @pytest.mark.parametrize("fmt,fmax,rel", [("e4m3fn", 448.0, 2.0 ** -4), ("e5m2", 57344.0, 2.0 ** -3)])
 def test_invariants(fmt, fmax, rel):
     rng = np.random.default_rng(2)
