@@ -19,6 +19,7 @@ ERR_BAD_DEVICE = -4
 ERR_WORKSPACE_TOO_SMALL = -5
 ERR_HIP = -6
 ERR_CAPTURE = -7
+ERR_TOO_LARGE = -8
 
 A_BF16 = 0
 A_E4M3 = 1
@@ -30,6 +31,8 @@ ACT_TABLE_BYTES = 131072
 
 FMT_E4M3FN = 0
 FMT_E5M2 = 1
+
+NOALLOC_SCRATCH_BYTES = 80 << 20
 
 MAX_ROWS = 1 << 24
 MAX_DIM = 1 << 20
@@ -51,6 +54,7 @@ SIGNATURES = {
     "fp8_linear_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.POINTER(_c_p)]),
     "fp8_linear_workspace_bytes": (ctypes.c_size_t, [_c_p, _c_i64]),
     "fp8_linear_run": (ctypes.c_int, [_c_p, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_linear_run_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p]),
     "fp8_linear_destroy": (None, [_c_p]),
     "fp8_linear": (ctypes.c_int, [_c_p, ctypes.c_int, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                   ctypes.c_size_t, _c_p]),

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <random>
 
 #include "internal.h"
@@ -222,6 +223,32 @@ int bucket_config(const Family& f, const int64_t* max_m, const int* config, int6
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The fixed scratch of fp8_linear_run_noalloc: a file-scope device array, one copy per
+// GPU, held from the library's first use on that GPU until the process ends. In host
+// code `scratch` is only a handle for the symbol lookup below, not a device address;
+// kernels get the per-device address that hipGetSymbolAddress returns.
+__device__ __align__(256) uint8_t scratch[FP8W8A8_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on `device`, which must be the current device; looked up
+// once per device (no allocation). NULL on failure.
+uint8_t* scratch_on(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  uint8_t* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[device].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = static_cast<uint8_t*>(addr);
+    g_scratch_ptr[device].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 // Launch epochs of the single-launch quant + GEMM: unique within the process (a
 // counter) and unlikely to repeat another process's (a random 64-bit start), so a
 // workspace's flags from any earlier launch never match the current one.
@@ -248,6 +275,7 @@ const char* fp8w8a8_status_string(int status) {
     case FP8W8A8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small: see fp8_linear_workspace_bytes";
     case FP8W8A8_ERR_HIP: return "HIP runtime error";
     case FP8W8A8_ERR_CAPTURE: return "not capturable: this call cannot be recorded into a HIP graph";
+    case FP8W8A8_ERR_TOO_LARGE: return "too large: the input exceeds FP8W8A8_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }
@@ -413,6 +441,23 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
   hipError_t e = launch_gemm(config, m, plan->n, plan->k, qa, sa, plan->w, plan->w_scale, plan->bias,
                              static_cast<uint16_t*>(out_bf16), s);
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_linear_run_noalloc(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind, const float* a_scale,
+                           void* out_bf16, void* stream) {
+  if (!plan || !a || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;
+  if (a_kind != FP8W8A8_A_BF16 && a_kind != FP8W8A8_A_E4M3) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (a_kind == FP8W8A8_A_E4M3)  // no scratch involved: exactly fp8_linear_run
+    return fp8_linear_run(plan, m, a, a_kind, a_scale, out_bf16, nullptr, 0, stream);
+  const size_t need = fp8_linear_workspace_bytes(plan, m);
+  if (need > FP8W8A8_NOALLOC_SCRATCH_BYTES) return FP8W8A8_ERR_TOO_LARGE;
+  if (m == 0) return FP8W8A8_OK;
+  int st = plan_device_current(plan->device);
+  if (st != FP8W8A8_OK) return st;
+  uint8_t* ws = scratch_on(plan->device);
+  if (!ws) return FP8W8A8_ERR_HIP;
+  return fp8_linear_run(plan, m, a, a_kind, a_scale, out_bf16, ws, need, stream);
 }
 
 void fp8_linear_destroy(fp8_linear_plan* plan) { free(plan); }

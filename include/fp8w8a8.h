@@ -61,6 +61,7 @@ extern "C" {
 #define FP8W8A8_ERR_WORKSPACE_TOO_SMALL (-5)  /* the workspace is smaller than fp8_linear_workspace_bytes */
 #define FP8W8A8_ERR_HIP (-6)                  /* a HIP runtime call or launch failed */
 #define FP8W8A8_ERR_CAPTURE (-7)              /* the call cannot be recorded into a HIP graph (fp8_quant_gemm) */
+#define FP8W8A8_ERR_TOO_LARGE (-8)            /* the input exceeds fp8_linear_run_noalloc's fixed scratch */
 
 /* ---- activation kinds for fp8_linear_run ------------------------------------ */
 #define FP8W8A8_A_BF16 0  /* a is bf16 [m, k]; the run quantises it per token into the workspace */
@@ -211,6 +212,30 @@ size_t fp8_linear_workspace_bytes(const fp8_linear_plan* plan, int64_t m);
 int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind,
                    const float* a_scale, void* out_bf16, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * fp8_linear_run_noalloc - fp8_linear_run without a workspace argument, for callers
+ * that cannot allocate device memory at all (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). A FP8W8A8_A_BF16 run quantises the
+ * activation into a fixed scratch array that the library holds in device memory, one
+ * per GPU, from the first call on that GPU until the process ends; nothing is
+ * allocated or freed by any call (the first call on a GPU only looks the array's
+ * address up). Same kernels, hence bit-identical output, as fp8_linear_run with a
+ * workspace.
+ *
+ *   plan, m, a, a_kind, a_scale, out_bf16, stream   as fp8_linear_run
+ * The codes and scales of m rows take fp8_linear_workspace_bytes(plan, m) bytes of the
+ * scratch; above FP8W8A8_NOALLOC_SCRATCH_BYTES the call returns FP8W8A8_ERR_TOO_LARGE
+ * and launches nothing (80 MiB holds, e.g., 4096 tokens of k = 8192 or 32760 tokens of
+ * k = 2048). FP8W8A8_A_E4M3 runs use no scratch and have no size limit beyond
+ * fp8_linear_run's. The scratch keeps the last call's codes; every BF16 run rewrites
+ * all the codes and scales its GEMM reads, so nothing needs clearing. All calls on
+ * one GPU share its scratch: two BF16 runs that overlap in time on the same GPU (for
+ * example on two streams) race, and the caller must order them.
+ */
+#define FP8W8A8_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+int fp8_linear_run_noalloc(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind,
+                           const float* a_scale, void* out_bf16, void* stream);
 
 /* Free a plan (NULL is ignored). Does not touch the borrowed device buffers. */
 void fp8_linear_destroy(fp8_linear_plan* plan);

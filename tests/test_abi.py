@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 def test_status_strings(lib):
     codes = [_lib.OK, _lib.ERR_INVALID_ARG, _lib.ERR_BAD_SHAPE, _lib.ERR_MISALIGNED, _lib.ERR_BAD_DEVICE,
-             _lib.ERR_WORKSPACE_TOO_SMALL, _lib.ERR_HIP, _lib.ERR_CAPTURE]
+             _lib.ERR_WORKSPACE_TOO_SMALL, _lib.ERR_HIP, _lib.ERR_CAPTURE, _lib.ERR_TOO_LARGE]
     texts = [lib.fp8w8a8_status_string(c).decode() for c in codes]
     assert len(set(texts)) == len(codes)
     assert lib.fp8w8a8_status_string(12345).decode() == "unknown status"
