@@ -3,7 +3,7 @@
 One step = the whole per-call hot path on one batch: dynamic per-token e4m3fn
 quantisation of the bf16 activation, then the FP8 GEMM with the fused
 activation-scale x weight-scale, bias and bf16 epilogue (two launches on one
-stream). The workload is the FFN-up linear of the HunyuanVideo1.5 DiT
+stream). The headline workload is the FFN-up linear of the HunyuanVideo1.5 DiT
 (M=4096 tokens, N=8192, K=2048). The weight is quantised per output channel and
 the plan built before timing (construction-time work, as the method prescribes).
 
@@ -14,35 +14,36 @@ operand is resident in HBM when the timed region starts.
 Prints one JSON line. `value` = 2 M N K / step time (TFLOP/s), from K steps timed
 with events only at the two ends of the region, after 0.3 s of untimed back-to-back
 steps (`preheat`: the clocks have dropped while the host built the inputs) and the W
-warm-up steps. `roofline` is the GEMM kernel (the
-dominant launch): its average launch duration comes from K launches of the GEMM
-alone, back to back with events on the launch stream at the two ends; the
-quantiser's launches are too short to be fed from Python one by one, so
-`quant.avg_launch_us` comes from K launches replayed from one HIP graph. A second
-region of K steps with an event around every launch gives each kernel's duration in
-its place in the step (`step_events_launch_us`: avg, p10, median, p90).
-`cpu_baseline` times the CPU oracle (numpy, float64) on the same workload.
+warm-up steps. `roofline` is the GEMM kernel (the dominant launch): its average launch
+duration comes from K launches of the GEMM alone, back to back with events on the
+launch stream at the two ends; the quantiser's launches are too short to be fed from
+Python one by one, so `quant.avg_launch_us` comes from K launches replayed from one HIP
+graph. A second region of K steps with an event around every launch gives each kernel's
+duration in its place in the step (`step_events_launch_us`: avg, p10, median, p90).
+`roofline.traffic` is the HBM bytes per launch from the committed rocprofv3 counter
+record, reported only while the GEMM's sources match the ones it was taken on.
+`cpu_baseline` times the CPU oracle (numpy, float64) on a bounded sample of the same
+workload.
 
-`w8a16` (outside the step) times the FP8 weight-only linear (bf16 activation x
-per-channel e4m3fn weight on the bf16 matrix cores) on the same FFN-up shape, against
-the dense bf16 MFMA peak.
+Other legs (outside the headline step; `--legs` selects them):
+  ffn_down      the FFN-down linear (M=4096, N=2048, K=8192, GELU(N(0,1)) input) as the
+                same kind of step, with its own roofline and quantiser records
+  quant_large   the per-token quantiser alone at [32760, 2048], [4096, 8192] and
+                [32760, 8192] (graph-replayed launches over rotating inputs and outputs)
+  w8a16         the FP8 weight-only linear (bf16 activation x per-channel e4m3fn weight
+                on the bf16 matrix cores) on the FFN-up shape, against the bf16 peak
+  producer      GELU (tanh form) -> per-token e4m3fn in one kernel against the unfused
+                pair, at [4096, 8192] and [32760, 8192]
+  tensor_quant  the per-tensor state-dict conversion (e4m3fn and e5m2) of [8192, 2048]
+                and [32760, 8192]
+  quant_gemm    the FFN-up step as one launch against the two-launch step
+  blocks        the QKV config (one quantisation of [32760, 2048], three GEMMs, the
+                26-row encoder input through the same weights) and the DiT block (4
+                quantisations, 6 GEMMs at 32760 tokens) as whole steps
+  cpu           the CPU oracle baseline
 
-`tensor_quant` (outside the step) times the per-tensor state-dict conversion (one
-scale per tensor, e4m3fn and e5m2) of the FFN-up weight [8192, 2048] and of the DiT
-FFN-down input size [32760, 8192]: an amax pass and a quantise pass over HBM.
-
-`producer` (outside the step) times the activation producer that feeds the
-FFN-down linear: GELU (tanh form) of the FFN-up output followed by per-token
-e4m3fn quantisation, fused in one kernel against the unfused pair (bf16 GELU
-output, then the plain quantiser), at the FFN-down input [4096, 8192] and at the
-DiT-block size [32760, 8192].
-
-`configs` (outside the step) times the QKV config (one quantisation of the [32760,
-2048] hidden input, three GEMMs, the 26-row encoder input through the same weights)
-and the DiT block (4 quantisations, 6 GEMMs at 32760 tokens) as whole steps.
-
-`clocks` reads the shader and memory clocks with amd-smi while the step runs back to
-back, and gives the GEMM's fraction of the dense-FP8 peak at that shader clock
+`clocks` reads the shader and memory clocks with amd-smi while the FFN-up step runs
+back to back, and gives the GEMM's fraction of the dense-FP8 peak at that shader clock
 (256 CUs x 8192 flop per clock) beside `roofline.frac`, which uses the published
 2.4 GHz peak.
 """
@@ -67,7 +68,7 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP8_FLOP_PER_CU_CLK = 8192  # dense FP8 MFMA per CU per shader clock (5.0 PFLOP/s = 256 CUs x 8192 x 2.4 GHz)
 N_CUS = 256
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_ffn_up_traffic.json")
+TRAFFIC_FILES = {name: os.path.join(ROOT, "profiles", f"gemm_fp8_{name}_traffic.json") for name in ("ffn_up", "ffn_down")}
 # the FP8 GEMM kernel's sources (the committed counter record names the SHA-256 over both)
 GEMM_SOURCES = [os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", f) for f in ("gemm_fp8.hip", "gemm_common.h")]
 
@@ -86,10 +87,10 @@ def quant_bytes(m, k):
     return 3 * m * k + 4 * m  # read bf16, write codes and fp32 scales
 
 
-def traffic_from_profile():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if still current."""
+def traffic_from_profile(path):
+    """HBM bytes per GEMM launch from a committed rocprofv3 counter record, if still current."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
         h = hashlib.sha256()
         for path in GEMM_SOURCES:
@@ -463,22 +464,258 @@ def cpu_baseline(budget_s=20.0):
     }
 
 
+# The two FFN linears of the block as timed steps (quantise + GEMM), each over its own
+# rotating sets: FFN-up is the headline workload, FFN-down (the GELU output as input, k =
+# 8192) the second shape the GEMM bar is quoted on.
+LINEAR_LEGS = {
+    "ffn_up": {
+        "M": 4096, "N": 8192, "K": 2048, "config_id": 2, "kind": "outlier", "sets": 16,
+        "workload": "FFN-up linear M4096 N8192 K2048: bf16 activation N(0,1) with 1% channels x50 -> "
+                    "per-token e4m3fn quant -> FP8 GEMM vs per-channel e4m3fn weight N(0,1/sqrt(2048)) "
+                    "-> x a_scale x w_scale + bf16 bias -> bf16",
+    },
+    "ffn_down": {
+        "M": 4096, "N": 2048, "K": 8192, "config_id": 3, "kind": "gelu", "sets": 12,
+        "workload": "FFN-down linear M4096 N2048 K8192: bf16 activation GELU(N(0,1)) -> per-token e4m3fn "
+                    "quant -> FP8 GEMM vs per-channel e4m3fn weight N(0,1/sqrt(8192)) -> x a_scale x w_scale "
+                    "+ bf16 bias -> bf16",
+    },
+}
+
+# Per-token quantiser at the large activation shapes of the configs: the QKV / DiT hidden
+# input, the FFN-down input at 4096 tokens, the DiT FFN-down input (rows, cols, kind,
+# config id, rotating sets; every set has its own input and its own code / scale buffers).
+QUANT_SHAPES = ((32760, 2048, "outlier", 4, 4), (4096, 8192, "gelu", 3, 8), (32760, 8192, "outlier", 5, 2))
+
+
+def _check_status(st, where):
+    if st:
+        from fp8_w8a8_quantized_token_amd import _lib
+        raise _lib.Fp8W8A8Error(st, where)
+
+
+def graph_avg(torch, dev, stream, fn, launches):
+    """`launches` calls of fn(i, stream_ptr) captured in one HIP graph and replayed once with
+    events at its two ends -> average duration per launch (ms). For launches too short to be
+    fed from Python one by one without the GPU waiting on the host in between."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn(0, ctypes.c_void_p(side.cuda_stream))
+    side.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        for i in range(launches):
+            fn(i, cap)
+    torch.cuda.synchronize()
+    g.replay()  # the first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / launches
+
+
+def back_to_back(torch, stream, fn, launches):
+    """`launches` calls of fn(i) with events on the launch stream at the two ends -> ms per call."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(launches):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches
+
+
+def linear_leg(torch, fp8, lib, dev, stream, name, steps, warmup, preheat_s, nsets=None, clocks=False):
+    """One FFN linear as a timed step: per-token quantisation of the bf16 activation, then the
+    plan's GEMM with the fused epilogue, over rotating input / weight / output sets."""
+    from fp8_w8a8_quantized_token_amd import _lib
+    from workloads.synth import activation, bias as gen_bias, outlier_channels, weight
+    spec = LINEAR_LEGS[name]
+    m, n, k, cid = spec["M"], spec["N"], spec["K"], spec["config_id"]
+    nsets = nsets or spec["sets"]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    ch = outlier_channels(0, cid, 0, k, None) if spec["kind"] == "outlier" else None
+    sets = []
+    for i in range(nsets):
+        a = activation(0, cid, 10 + i, m, k, spec["kind"], ch).to(dev)
+        w = weight(0, cid, 100 + i, n, k).to(dev)
+        b = gen_bias(0, cid, 200 + i, n).to(dev)
+        lin = fp8.Fp8Linear(w, b)  # per-channel weight quant + plan: construction time
+        del w
+        q = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((m,), dtype=torch.float32, device=dev)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        sets.append((a, q, s, lin, out))
+    torch.cuda.synchronize()
+    config = sets[0][3].config(m)
+
+    def quant_only(i, on=sptr):
+        a, q, s, lin, out = sets[i % nsets]
+        _check_status(lib.fp8_quant_rows(P(a), m, k, P(q), P(s), on), "fp8_quant_rows")
+
+    def gemm_only(i):
+        a, q, s, lin, out = sets[i % nsets]
+        _check_status(lib.fp8_linear_run(lin._plan, m, P(q), _lib.A_E4M3, P(s), P(out), None, 0, sptr),
+                      "fp8_linear_run")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        quant_only(i)
+        if ev is not None:
+            ev[1].record(stream)
+        gemm_only(i)
+        if ev is not None:
+            ev[2].record(stream)
+
+    # Pre-heat: after the host-side set-up the GPU has idled and its clocks have dropped;
+    # without this the first few milliseconds of steps run while they ramp back up.
+    t_pre = time.perf_counter()
+    preheat_steps = preheat(torch, step, preheat_s, batch=50)
+    preheat_wall = time.perf_counter() - t_pre
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region 1: exactly K steps, events only at its ends -> ms_per_step, value.
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+
+    # Timed region 2: the same K steps with an event on the launch stream around every
+    # launch -> each kernel's launch duration inside the step (avg, p10 / median / p90).
+    # An event between two launches adds a wait of its own to the interval it closes.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    quant_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    gemm_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+
+    # Timed regions 3 and 4: K launches of each kernel alone over the same rotating sets,
+    # events on the launch stream at the two ends only -> each kernel's average launch
+    # duration (the roofline figures). The GEMM's launches go back to back from Python;
+    # the quantiser's are replayed from one graph.
+    g_avg = back_to_back(torch, stream, gemm_only, steps)
+    q_avg_eager = back_to_back(torch, stream, quant_only, steps)
+    q_avg = graph_avg(torch, dev, stream, quant_only, steps)
+
+    clk = sample_clocks(torch, step) if clocks else None
+    flop = 2.0 * m * n * k
+    gemm_tflops = flop / (g_avg * 1e-3) / 1e12
+    res = {
+        "workload": spec["workload"], "M": m, "N": n, "K": k, "rotating_sets": nsets,
+        "gemm_config": {"id": config[0], "tile_m": config[1], "tile_n": config[2], "workgroups": config[3]},
+        "preheat": {"seconds": round(preheat_wall, 3), "steps": preheat_steps},
+        "steps": steps, "ms_per_step": round(ms_per_step, 5),
+        "tflops": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_fp8_kernel",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic_from_profile(TRAFFIC_FILES[name]),
+            "avg_launch_us": round(g_avg * 1e3, 3),
+            "avg_launch_us_source": "K GEMM launches back to back, events at the two ends",
+            "algorithmic_flop_per_launch": flop,
+            "algorithmic_bytes_per_launch": gemm_bytes(m, n, k),
+            "step_events_launch_us": {"avg": round(sum(gemm_ms) / len(gemm_ms) * 1e3, 3),
+                                      "p10": round(pct(gemm_ms, 10) * 1e3, 3),
+                                      "median": round(pct(gemm_ms, 50) * 1e3, 3),
+                                      "p90": round(pct(gemm_ms, 90) * 1e3, 3)},
+        },
+        "quant": {
+            "kernel": "quant_rows_regs" if k <= 2048 else "quant_rows_split",
+            "avg_launch_us": round(q_avg * 1e3, 3),
+            "avg_launch_us_source": "K launches replayed from one HIP graph, events at the two ends",
+            "avg_launch_us_eager_back_to_back": round(q_avg_eager * 1e3, 3),
+            "step_events_launch_us": {"avg": round(sum(quant_ms) / len(quant_ms) * 1e3, 3),
+                                      "p10": round(pct(quant_ms, 10) * 1e3, 3),
+                                      "median": round(pct(quant_ms, 50) * 1e3, 3),
+                                      "p90": round(pct(quant_ms, 90) * 1e3, 3)},
+            "gbps": round(quant_bytes(m, k) / (q_avg * 1e-3) / 1e9, 1),
+            "frac_hbm": round(quant_bytes(m, k) / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes_per_launch": quant_bytes(m, k),
+        },
+    }
+    if clk is not None:
+        # Peak at the clock the chip actually ran: 256 CUs x 8192 FP8 flop per CU per clock.
+        sclk_peak = N_CUS * FP8_FLOP_PER_CU_CLK * clk["sclk_mhz"] * 1e6 / 1e12
+        clk["gemm_peak_at_sclk_tflops"] = round(sclk_peak, 1)
+        clk["gemm_frac_at_sclk"] = round(gemm_tflops / sclk_peak, 4)
+    res["clocks"] = clk
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def quant_large_bench(torch, lib, dev, stream, steps):
+    """Per-token quantiser alone at the large activation shapes: K launches replayed from one
+    HIP graph over rotating inputs and outputs, events at the two ends."""
+    from workloads.synth import activation, outlier_channels
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = {"kernel": "quant_rows_regs / quant_rows_split", "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "shapes": []}
+    for rows, cols, kind, cid, nsets in QUANT_SHAPES:
+        ch = outlier_channels(0, cid, 0, cols, None) if kind == "outlier" else None
+        bufs = []
+        for i in range(nsets):
+            x = activation(0, cid, 30 + i, rows, cols, kind, ch).to(dev)
+            q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+            s = torch.empty((rows,), dtype=torch.float32, device=dev)
+            bufs.append((x, q, s))
+        torch.cuda.synchronize()
+
+        def run(i, on):
+            x, q, s = bufs[i % nsets]
+            _check_status(lib.fp8_quant_rows(P(x), rows, cols, P(q), P(s), on), "fp8_quant_rows")
+
+        sptr = ctypes.c_void_p(stream.cuda_stream)
+        preheat(torch, lambda i: run(i, sptr))
+        ms = graph_avg(torch, dev, stream, run, steps)
+        algo = quant_bytes(rows, cols)
+        gbps = algo / (ms * 1e-3) / 1e9
+        out["shapes"].append({"rows": rows, "cols": cols, "input": kind, "rotating_sets": nsets,
+                              "avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes_per_launch": algo,
+                              "achieved": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)})
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+LEGS = ("ffn_up", "ffn_down", "quant_large", "w8a16", "producer", "tensor_quant", "quant_gemm", "blocks", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=16, help="rotating input/weight/output sets")
+    ap.add_argument("--sets", type=int, default=None, help="rotating input/weight/output sets of the FFN legs")
     ap.add_argument("--preheat-s", type=float, default=0.3,
                     help="seconds of back-to-back steps before the warm-up steps, so the timed steps run at "
                          "the clocks the chip holds under this load rather than while it ramps up from idle")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated legs to run (default: all); without ffn_up the line carries only the "
+                         f"legs' records (for kernel profiles). Legs: {', '.join(LEGS)}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock samples")
-    ap.add_argument("--no-producer", action="store_true", help="skip the GELU -> FP8 producer timing")
-    ap.add_argument("--no-w8a16", action="store_true", help="skip the FP8 weight-only linear timing")
-    ap.add_argument("--no-tensor-quant", action="store_true", help="skip the per-tensor quantisation timing")
-    ap.add_argument("--no-quant-gemm", action="store_true", help="skip the single-launch quant + GEMM timing")
-    ap.add_argument("--no-blocks", action="store_true", help="skip the whole-config (QKV, DiT block) timings")
     ap.add_argument("--producer-only", type=int, metavar="ROWS", choices=[r for r, _, _ in PRODUCER_SHAPES],
                     help="time only the producer, at one row count (for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -489,18 +726,22 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(tokens would shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    legs = [x.strip() for x in args.legs.split(",") if x.strip()]
+    unknown = [x for x in legs if x not in LEGS]
+    if unknown:
+        ap.error(f"unknown legs {unknown}; choose from {LEGS}")
+    if args.no_cpu_baseline and "cpu" in legs:
+        legs.remove("cpu")
 
     import torch
     import fp8_w8a8_quantized_token_amd as fp8
     from fp8_w8a8_quantized_token_amd import _lib
-    from workloads.synth import activation, bias as gen_bias, outlier_channels, weight
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
     lib = _lib.lib()
     stream = torch.cuda.current_stream(dev)
-    sptr = ctypes.c_void_p(stream.cuda_stream)
 
     if args.producer_only:
         res = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)), args.producer_only)
@@ -510,213 +751,54 @@ def main():
         print(json.dumps({"producer": res}), flush=True)
         return
 
-    # rotating sets: activation bf16, codes + scales, weight plan, output
-    sets = []
-    ch = outlier_channels(0, 2, 0, K, None)
-    for i in range(args.sets):
-        a = activation(0, 2, 10 + i, M, K, "outlier", ch).to(dev)
-        w = weight(0, 2, 100 + i, N, K).to(dev)
-        b = gen_bias(0, 2, 200 + i, N).to(dev)
-        lin = fp8.Fp8Linear(w, b)  # per-channel weight quant + plan: construction time
-        del w
-        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
-        s = torch.empty((M,), dtype=torch.float32, device=dev)
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        sets.append((a, q, s, lin, out))
-    torch.cuda.synchronize()
-    config = sets[0][3].config(M)
-
-    def step(i, ev=None):
-        a, q, s, lin, out = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
-        st = lib.fp8_quant_rows(ctypes.c_void_p(a.data_ptr()), M, K, ctypes.c_void_p(q.data_ptr()),
-                                ctypes.c_void_p(s.data_ptr()), sptr)
-        if st:
-            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
-        if ev is not None:
-            ev[1].record(stream)
-        st = lib.fp8_linear_run(lin._plan, M, ctypes.c_void_p(q.data_ptr()), _lib.A_E4M3,
-                                ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(out.data_ptr()), None, 0, sptr)
-        if st:
-            raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
-        if ev is not None:
-            ev[2].record(stream)
-
-    # Pre-heat: after the host-side set-up the GPU has idled and its clocks have dropped;
-    # without this the first few milliseconds of steps run while they ramp back up.
-    t_pre = time.perf_counter()
-    preheat_steps = preheat(torch, step, args.preheat_s, batch=50)
-    preheat_s = time.perf_counter() - t_pre
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region 1: exactly K steps, events only at its ends -> ms_per_step, value.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-
-    # Timed region 2: the same K steps with an event on the launch stream around every
-    # launch -> each kernel's launch duration inside the step (avg, p10 / median / p90).
-    # An event between two launches adds a wait of its own to the interval it closes.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-
-    # Timed regions 3 and 4: K launches of each kernel alone over the same rotating sets,
-    # events on the launch stream at the two ends only -> each kernel's average launch
-    # duration (the roofline figures). The GEMM's launches go back to back; the
-    # quantiser's are too short to be fed from Python one by one, so they are replayed
-    # from one graph.
-    def gemm_only(i):
-        a, q, s, lin, out = sets[i % len(sets)]
-        st = lib.fp8_linear_run(lin._plan, M, ctypes.c_void_p(q.data_ptr()), _lib.A_E4M3,
-                                ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(out.data_ptr()), None, 0, sptr)
-        if st:
-            raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
-
-    def quant_only(i, on=sptr):
-        a, q, s, lin, out = sets[i % len(sets)]
-        st = lib.fp8_quant_rows(ctypes.c_void_p(a.data_ptr()), M, K, ctypes.c_void_p(q.data_ptr()),
-                                ctypes.c_void_p(s.data_ptr()), on)
-        if st:
-            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
-
-    def graph_avg(fn):
-        """K launches captured in one HIP graph, replayed with events at its two ends: the
-        quantiser's launches are short enough that eager launches from Python leave the GPU
-        waiting on the host between them."""
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            fn(0, ctypes.c_void_p(side.cuda_stream))
-        side.synchronize()
-        with torch.cuda.graph(g, stream=side):
-            cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-            for i in range(args.steps):
-                fn(i, cap)
-        torch.cuda.synchronize()
-        g.replay()  # first replay uploads the graph
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) / args.steps
-
-    def back_to_back(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    g_avg = back_to_back(gemm_only)
-    q_avg_eager = back_to_back(quant_only)
-    q_avg = graph_avg(quant_only)
-
-    clocks = None if args.no_clocks else sample_clocks(torch, step)
-
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    quant_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    gemm_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    flop = 2.0 * M * N * K
-    value = flop / (ms_per_step * 1e-3) / 1e12
-    gemm_tflops = flop / (g_avg * 1e-3) / 1e12
-    traffic = traffic_from_profile()
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "preheat": {"seconds": round(preheat_s, 3), "steps": preheat_steps},
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
-        "data": "synthetic",
-        "config": {
-            "workload": "FFN-up linear M4096 N8192 K2048: bf16 activation N(0,1) with 1% channels x50 -> "
-                        "per-token e4m3fn quant -> FP8 GEMM vs per-channel e4m3fn weight N(0,1/sqrt(2048)) "
-                        "-> x a_scale x w_scale + bf16 bias -> bf16",
-            "M": M, "N": N, "K": K,
-            "rotating_sets": args.sets,
-            "gemm_config": {"id": config[0], "tile_m": config[1], "tile_n": config[2], "workgroups": config[3]},
-        },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "gemm_fp8_kernel",
-            "achieved": round(gemm_tflops, 2),
-            "peak": PEAK_FP8_TFLOPS,
+    result = {}
+    if "ffn_up" in legs:
+        up = linear_leg(torch, fp8, lib, dev, stream, "ffn_up", args.steps, args.warmup, args.preheat_s, args.sets,
+                        clocks=not args.no_clocks)
+        m, n, k = up["M"], up["N"], up["K"]
+        result = {
+            "metric": METRIC,
+            "value": up["tflops"],
             "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": traffic,
-            "avg_launch_us": round(g_avg * 1e3, 3),
-            "avg_launch_us_source": "K GEMM launches back to back, events at the two ends",
-            "algorithmic_flop_per_launch": flop,
-            "algorithmic_bytes_per_launch": gemm_bytes(M, N, K),
-            "step_events_launch_us": {"avg": round(sum(gemm_ms) / len(gemm_ms) * 1e3, 3),
-                                      "p10": round(pct(gemm_ms, 10) * 1e3, 3),
-                                      "median": round(pct(gemm_ms, 50) * 1e3, 3),
-                                      "p90": round(pct(gemm_ms, 90) * 1e3, 3)},
-        },
-        "quant": {
-            "kernel": "quant_rows_regs",
-            "avg_launch_us": round(q_avg * 1e3, 3),
-            "avg_launch_us_source": "K launches replayed from one HIP graph, events at the two ends",
-            "avg_launch_us_eager_back_to_back": round(q_avg_eager * 1e3, 3),
-            "step_events_launch_us": {"avg": round(sum(quant_ms) / len(quant_ms) * 1e3, 3),
-                                      "p10": round(pct(quant_ms, 10) * 1e3, 3),
-                                      "median": round(pct(quant_ms, 50) * 1e3, 3),
-                                      "p90": round(pct(quant_ms, 90) * 1e3, 3)},
-            "gbps": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9, 1),
-            "frac_hbm": round(quant_bytes(M, K) / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "algorithmic_bytes_per_launch": quant_bytes(M, K),
-        },
-    }
-    if clocks is not None:
-        # Peak at the clock the chip actually ran: 256 CUs x 8192 FP8 flop per CU per clock.
-        sclk_peak = N_CUS * FP8_FLOP_PER_CU_CLK * clocks["sclk_mhz"] * 1e6 / 1e12
-        clocks["gemm_peak_at_sclk_tflops"] = round(sclk_peak, 1)
-        clocks["gemm_frac_at_sclk"] = round(gemm_tflops / sclk_peak, 4)
-    result["clocks"] = clocks
-    del sets
-    torch.cuda.empty_cache()
-    if not args.no_w8a16:
-        result["w8a16"] = w8a16_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
-    if not args.no_producer:
-        result["producer"] = producer_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
-    if not args.no_tensor_quant:
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "preheat": up["preheat"],
+            "ms_per_step": up["ms_per_step"],
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
+            "data": "synthetic",
+            "config": {"workload": up["workload"], "M": m, "N": n, "K": k, "rotating_sets": up["rotating_sets"],
+                       "gemm_config": up["gemm_config"]},
+            "roofline": up["roofline"],
+            "quant": up["quant"],
+            "clocks": up["clocks"],
+        }
+    short = max(10, min(args.steps, 100))
+    if "ffn_down" in legs:
+        down = linear_leg(torch, fp8, lib, dev, stream, "ffn_down", args.steps, args.warmup, args.preheat_s,
+                          args.sets, clocks=False)
+        down.pop("clocks", None)
+        result["ffn_down"] = down
+    if "quant_large" in legs:
+        result["quant_large"] = quant_large_bench(torch, lib, dev, stream, short)
+    if "w8a16" in legs:
+        result["w8a16"] = w8a16_bench(torch, fp8, lib, dev, stream, short)
+    if "producer" in legs:
+        result["producer"] = producer_bench(torch, fp8, lib, dev, stream, short)
+    if "tensor_quant" in legs:
         result["tensor_quant"] = tensor_quant_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 50)))
-    if not args.no_quant_gemm:
-        result["quant_gemm"] = quant_gemm_bench(torch, fp8, lib, dev, stream, max(10, min(args.steps, 100)))
-    if not args.no_blocks:
+    if "quant_gemm" in legs:
+        result["quant_gemm"] = quant_gemm_bench(torch, fp8, lib, dev, stream, short)
+    if "blocks" in legs:
         result["configs"] = {name: block_bench(torch, fp8, lib, dev, stream, max(5, min(args.steps, 20)), name)
                              for name in ("qkv", "dit_block")}
     if args.copy_calibration:
         copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30, "launches": 3}
-    if not args.no_cpu_baseline:
+    if "cpu" in legs:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 

@@ -74,3 +74,57 @@ def test_committed_traffic_record_is_well_formed():
     t = json.load(open(os.path.join(root, "profiles", "gemm_fp8_ffn_up_traffic.json")))
     assert t["hbm_bytes_per_launch"] == pytest.approx(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
     assert t["launches"] > 0 and len(t["source_sha256"]) == 64
+
+
+def _write_counters(path, counter, launches):
+    """launches: (kernel name, grid size, value KiB)."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, grid, v in launches:
+            w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_traffic_groups_launches_by_grid_size(tmp_path):
+    # one kernel at two shapes (as the quantiser runs on activations and weights): each shape
+    # gets its own median, scaled by the 1 GiB copy's reading, with its algorithmic ratio
+    cal = [("__amd_rocclr_copyBuffer", 1 << 20, 524288.0)] * 3
+    fetch = cal + [("quant_rows_regs<2>", 262144, 16384.0)] * 5 + [("quant_rows_regs<2>", 524288, 32768.0)] * 4
+    write = [(n, g, 2 * v if "copy" in n else v / 2) for n, g, v in fetch]
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_counters(fp, "FETCH_SIZE", fetch)
+    _write_counters(wp, "WRITE_SIZE", write)
+    t = profiling.traffic(str(fp), str(wp), "quant_rows", groups={524288: (50e6, "weights")})
+    assert [g["grid_size"] for g in t["groups"]] == [524288, 262144]
+    w, a = t["groups"]
+    assert w["launches"] == 4 and a["launches"] == 5
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    assert w["fetch_bytes_per_launch"] == pytest.approx(32768 * 1024 * 2)
+    assert w["write_bytes_per_launch"] == pytest.approx(16384 * 1024)
+    assert w["traffic_over_algorithmic"] == pytest.approx((64 + 16) * 1024 * 1024 / 50e6)
+    assert t["hbm_bytes_per_launch"] == w["hbm_bytes_per_launch"]
+    text = profiling.traffic_markdown(t, "cmd")
+    assert "| weights | 524288 | 4 |" in text and "| - | 262144 | 5 |" in text
+
+
+def test_counters_mfma_busy_share(tmp_path):
+    # 3 launches of one shape: GUI-active summed over 8 XCDs, MFMA busy summed over 1024 SIMDs
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d in range(3):
+            row = {"Dispatch_Id": d, "Kernel_Name": "gemm<false>", "Grid_Size": 262144,
+                   "Start_Timestamp": 1000, "End_Timestamp": 1000 + 50_000}
+            w.writerow(dict(row, Counter_Name="GRBM_GUI_ACTIVE", Counter_Value=8 * 100_000))
+            w.writerow(dict(row, Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES", Counter_Value=1024 * 60_000))
+            w.writerow(dict(row, Counter_Name="SQ_INSTS_VALU_MFMA_MOPS_F8", Counter_Value=1_000_000))
+    recs = profiling.counters(str(p), "gemm", {262144: (5.12e8, "FFN-up")})
+    assert len(recs) == 1
+    r = recs[0]
+    assert r["launches"] == 3 and r["label"] == "FFN-up"
+    assert r["mfma_busy"] == pytest.approx(0.6)
+    assert r["mfma_flop"] == pytest.approx(5.12e8)
+    assert r["duration_us"] == pytest.approx(50.0) and r["gui_clock_ghz"] == pytest.approx(2.0)
+    assert "| matrix-core busy share" in profiling.counters_markdown(recs, "cmd")
