@@ -38,7 +38,7 @@ struct GemmConfig {
   int tile_m;   // block rows along m (activation rows)
   int tile_n;   // block columns along n (weight rows / output channels)
   int waves;    // 64-lane wavefronts per workgroup
-  int stages;   // LDS pipeline depth (64 bytes of k per stage)
+  int stages;   // LDS pipeline depth (128 bytes of k per stage)
   const char* name;
 };
 
