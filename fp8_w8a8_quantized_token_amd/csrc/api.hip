@@ -157,20 +157,29 @@ struct Family {
   int64_t (*workgroups)(int, int64_t, int64_t);
   int (*threads)(int);
   TileModel (*model)(int);
+  int skinny;           // configuration for m <= skinny_max_m (outside the tile model), or -1
+  int64_t skinny_max_m;
 };
 // m buckets: rows <= bound[b] use the configuration chosen at that bound; the last bucket
 // is unbounded and chosen at 32768 rows. The W8A8 model picks the measured best on all 17
 // timed shapes with these bounds; the W8A16 model, which has no fixed-cost term, needs the
 // finer powers of two (with the coarse bounds it kept 128 x 256 tiles at 512 x 8192 x 2048
 // and 2048 x 2048 x 8192, 13% and 11% slower than 128 x 128 there).
-constexpr int64_t kW8A8Bounds[] = {64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
+constexpr int64_t kW8A8Bounds[] = {32, 64, 256, 1024, 4096, 16384, FP8W8A8_MAX_ROWS};
 constexpr int64_t kW8A16Bounds[] = {64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, FP8W8A8_MAX_ROWS};
 static_assert(sizeof(kW8A8Bounds) / sizeof(int64_t) <= kMaxBuckets, "bucket count");
 static_assert(sizeof(kW8A16Bounds) / sizeof(int64_t) <= kMaxBuckets, "bucket count");
+// The skinny W8A8 configuration (one workgroup per 16 channels, k split across its waves)
+// is a weight stream, not a tile of the model above. Timed against the 64 x 64 tiles
+// (graph-replayed launches, random codes, rotating weights): m = 26 at n x k = 2048 x 2048
+// 5.4 against 9.1 us, 8192 x 2048 7.9 against 9.3, 2048 x 8192 12.7 against 25.8; m = 1
+// 4.0 against 9.0. Above 32 tokens it loads the weight once per 32 tokens and loses at
+// wide n (m = 64, n = 8192: 14.8 against 9.6 us), so it serves m <= 32 only.
+constexpr int kW8A8Skinny = 5;
 const Family kW8A8{kW8A8Bounds, (int)(sizeof(kW8A8Bounds) / sizeof(int64_t)), gemm_config_count, gemm_config,
-                   gemm_workgroups, gemm_threads, w8a8_tile_model};
+                   gemm_workgroups, gemm_threads, w8a8_tile_model, kW8A8Skinny, 32};
 const Family kW8A16{kW8A16Bounds, (int)(sizeof(kW8A16Bounds) / sizeof(int64_t)), w8a16_config_count, w8a16_config,
-                    w8a16_workgroups, w8a16_threads, w8a16_tile_model};
+                    w8a16_workgroups, w8a16_threads, w8a16_tile_model, -1, 0};
 
 bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
   return f.workgroups(config, m, n) * f.threads(config) < kMaxGridThreads;
@@ -191,10 +200,11 @@ double model_time(const Family& f, int c, int64_t m, int64_t n, int64_t k, int c
 }
 
 int choose_config(const Family& f, int64_t m, int64_t n, int64_t k, int cus) {
+  if (f.skinny >= 0 && m <= f.skinny_max_m && grid_fits(f, f.skinny, m, n)) return f.skinny;
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < f.count(); ++c) {
-    if (!grid_fits(f, c, m, n)) continue;
+    if (c == f.skinny || !grid_fits(f, c, m, n)) continue;
     const double t = model_time(f, c, m, n, k, cus);
     if (best < 0 || t < best_t) {
       best = c;

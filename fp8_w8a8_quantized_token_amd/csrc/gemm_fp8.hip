@@ -45,6 +45,9 @@
 //     shares holding its tile's tokens, then runs
 //     its tile as above. The weight half of the first stages is requested before the
 //     quantisation so it lands meanwhile.
+//   * A skinny form for a few dozen tokens (the 26-row encoder input of the QKV
+//     projections): a weight stream over many workgroups with k split across waves and
+//     operands loaded straight into registers (gemm_fp8_skinny below).
 #include <algorithm>
 
 #include "internal.h"
@@ -529,6 +532,153 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---- skinny form: few tokens (the 26-row encoder input of the QKV projections) ----------
+//
+// With m of a few dozen the product is a stream of the weight through the chip: 2 m n k
+// flop against n k bytes of weight, far below any matrix-core limit. What bounds it is
+// how many CUs pull weight bytes at once and how much else each of them must load. The
+// tiled kernel's smallest tile (64 x 64) gives one workgroup per 64 channels (32 for
+// n = 2048) that walks k through a three-stage LDS pipeline, so most CUs idle and each
+// active one waits on a chain of dependent stages. Here a workgroup owns NW = 16 channels
+// and 16 * MT tokens (grid: ceil(n / 16) x ceil(m / (16 MT)) workgroups, 128 for the
+// encoder GEMM), and its WAVES waves split k between them: wave w takes the 128-byte
+// k-steps w, w + WAVES, ... . Each wave loads its operand fragments straight from
+// memory into registers (no LDS staging, no barrier in the loop), two k-steps per batch
+// with the next batch requested before the current one is multiplied, and runs
+// V_MFMA_F32_16X16X128_F8F6F4 on them. The waves' partial sums meet in LDS once; the
+// sum over waves is taken in a fixed order and the epilogue (fp32, one rounding to bf16)
+// follows the tiled kernel's. Out-of-range rows and k-chunks read zeros through the
+// buffer descriptors, as in the tiled kernel.
+//
+// Operand layout of the 16x16x128 MFMA: lane l holds row l % 16 of the 16-row operand
+// and 32 bytes of its k; the two operands must agree on which k those are. Here lane
+// l holds k bytes [16 q, 16 q + 16) and [64 + 16 q, 64 + 16 q + 16) of the step, q = l / 16,
+// so each of the two 16-byte loads of a fragment reads the first or second half of
+// every row's 128-byte line. Results: lane l holds column l % 16 (token) and rows
+// 4 (l / 16) + i (channels), i = 0..3.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kSkinnyNW = 16;     // channels per workgroup
+constexpr int kSkinnyWaves = 8;   // waves per workgroup, splitting k
+constexpr int kSkinnyBatch = 2;   // 128-byte k-steps per load batch
+
+template <int MT>
+struct SkinnyFrags {
+  v8i w[kSkinnyBatch];
+  v8i a[kSkinnyBatch][MT];
+};
+
+template <int MT>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs args) {
+  constexpr int WAVES = kSkinnyWaves;
+  constexpr int TM = 16 * MT;  // tokens per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tn = blockIdx.x % args.tiles_n, tm = blockIdx.x / args.tiles_n;
+  const int n0 = tn * kSkinnyNW, m0 = tm * TM;
+  const int K = args.k;
+  const int rows_a = min(TM, args.m - m0);
+  const int rows_w = min(kSkinnyNW, args.n - n0);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qa) + (int64_t)m0 * K, 0,
+                                        (uint32_t)rows_a * (uint32_t)K, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qw) + (int64_t)n0 * K, 0,
+                                        (uint32_t)rows_w * (uint32_t)K, kBufferConfig);
+
+  // epilogue operands of this thread's output (token t / 16, channel t % 16), requested now
+  const int et = threadIdx.x / kSkinnyNW, ec = threadIdx.x % kSkinnyNW;
+  const bool evalid = et < rows_a && ec < rows_w;
+  float e_sa = 0.0f, e_sw = 0.0f, e_b = 0.0f;
+  if (evalid) {
+    e_sa = args.a_scale[m0 + et];
+    e_sw = args.w_scale[n0 + ec];
+    if (args.bias) e_b = __uint_as_float((uint32_t)args.bias[n0 + ec] << 16);
+  }
+
+  const int r = lane & 15, q = lane >> 4;
+  const uint32_t row_off = (uint32_t)r * (uint32_t)K;
+  const int steps = (K + 127) / 128;
+  auto load = [&](int step, v8i& w, v8i* a) {
+    // chunk c of the step's 128 bytes holds k bytes [16 c, 16 c + 16); lanes past k read zeros
+    const int k0 = step * 128 + 16 * q, k1 = k0 + 64;
+    const uint32_t o0 = k0 < K ? row_off + (uint32_t)k0 : kOutOfRange;
+    const uint32_t o1 = k1 < K ? row_off + (uint32_t)k1 : kOutOfRange;
+    const v4u w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o0, 0, 0);
+    const v4u w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o1, 0, 0);
+    w = v8i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t d = (uint32_t)(16 * t) * (uint32_t)K;
+      const v4u a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, o0 == kOutOfRange ? o0 : o0 + d, 0, 0);
+      const v4u a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, o1 == kOutOfRange ? o1 : o1 + d, 0, 0);
+      a[t] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    }
+  };
+  auto load_batch = [&](int first, SkinnyFrags<MT>& f) {
+#pragma unroll
+    for (int b = 0; b < kSkinnyBatch; ++b) {
+      const int step = first + b * WAVES;
+      if (step < steps) load(step, f.w[b], f.a[b]);
+    }
+  };
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto mfma_batch = [&](int first, const SkinnyFrags<MT>& f) {
+#pragma unroll
+    for (int b = 0; b < kSkinnyBatch; ++b)
+      if (first + b * WAVES < steps)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.w[b], f.a[b][t], acc[t], 0, 0, 0, 0, 0, 0);
+  };
+
+  constexpr int kStride = kSkinnyBatch * WAVES;  // k-steps between a wave's batches
+  SkinnyFrags<MT> f0, f1;
+  load_batch(wave, f0);
+  for (int s = wave; s < steps; s += 2 * kStride) {
+    load_batch(s + kStride, f1);
+    mfma_batch(s, f0);
+    if (s + kStride >= steps) break;
+    load_batch(s + 2 * kStride, f0);
+    mfma_batch(s + kStride, f1);
+  }
+
+  // partial sums of every wave -> LDS, then a fixed-order sum per output
+  __shared__ v4f red[WAVES][MT][64];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int o = threadIdx.x; o < TM * kSkinnyNW; o += WAVES * 64) {
+    const int tok = o / kSkinnyNW, ch = o % kSkinnyNW;
+    // token tok is column tok % 16 of m-tile tok / 16; channel ch is row ch of the result
+    const int src_lane = (tok & 15) + 16 * (ch >> 2);
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][tok >> 4][src_lane][ch & 3];
+    if (tok < rows_a && ch < rows_w) {
+      const float sa = o == (int)threadIdx.x ? e_sa : args.a_scale[m0 + tok];
+      const float sw = o == (int)threadIdx.x ? e_sw : args.w_scale[n0 + ch];
+      const float b = o == (int)threadIdx.x ? e_b : (args.bias ? __uint_as_float((uint32_t)args.bias[n0 + ch] << 16) : 0.0f);
+      const float v = __builtin_fmaf(sum * sa, sw, b);
+      args.out[(int64_t)(m0 + tok) * args.n + n0 + ch] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    }
+  }
+  (void)evalid;
+}
+
+template <int MT>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
+  GemmArgs args = a;
+  args.tiles_n = (a.n + kSkinnyNW - 1) / kSkinnyNW;
+  args.tiles_m = (a.m + 16 * MT - 1) / (16 * MT);
+  const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
+  gemm_fp8_skinny<MT><<<dim3((unsigned)wgs), dim3(kSkinnyWaves * 64), 0, stream>>>(args);
+  return hipGetLastError();
+}
+
 // id, tile_m, tile_n, waves, stages, name (every stage holds 128 bytes of k)
 const GemmConfig kConfigs[] = {
     {0, 256, 256, 8, 2, "bm256_bn256_w2x4_s2"},
@@ -536,6 +686,7 @@ const GemmConfig kConfigs[] = {
     {2, 128, 256, 8, 3, "bm128_bn256_w2x4_s3"},
     {3, 128, 128, 4, 2, "bm128_bn128_w2x2_s2"},
     {4, 64, 64, 4, 3, "bm64_bn64_w2x2_s3"},
+    {5, 32, 16, 8, 0, "skinny_m32_n16_w8"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -566,6 +717,7 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 2: return launch<128, 256, 2, 4, 3, 128, 8>(a, stream);  // groups of 8: FFN-down 64.3 -> 63.4 us
     case 3: return launch<128, 128, 2, 2, 2, 128, 8>(a, stream);
     case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
+    case 5: return launch_skinny<2>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

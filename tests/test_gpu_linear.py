@@ -237,8 +237,9 @@ def test_selector_is_fixed_at_construction():
 
 
 def test_selector_picks_the_measured_best_at_the_page_shapes():
-    # 256 x 256 tiles for FFN-up and the 32760-token layers, 128 x 256 for FFN-down, 64 x 64
-    # for the 26-row encoder input: the fastest configuration at each when timed on MI355X
+    # 256 x 256 tiles for FFN-up and the 32760-token layers, 128 x 256 for FFN-down, the
+    # skinny weight stream for the 26-row encoder input: the fastest configuration at each
+    # when timed on MI355X
     dev = require_gpu()
     if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
         pytest.skip("the picks are measured for a 256-CU device")
@@ -248,7 +249,8 @@ def test_selector_picks_the_measured_best_at_the_page_shapes():
     assert up.config(4096)[0] == 0
     assert down.config(4096)[0] == 2
     assert qkv.config(32760)[0] == 0 and down.config(32760)[0] == 0
-    assert qkv.config(26)[0] == 4
+    assert qkv.config(26)[0] == 5 and up.config(26)[0] == 5 and down.config(26)[0] == 5
+    assert qkv.config(64)[0] == 4
 
 
 def test_errors_are_statuses_not_crashes():
