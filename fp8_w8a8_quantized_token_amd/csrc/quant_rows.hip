@@ -33,29 +33,32 @@ __global__ __launch_bounds__(kBlock) void quant_rows_regs(const uint16_t* __rest
   qrow::quant_row<NC>(va, vb, nchunks, lane, q + row * cols, scale + row);
 }
 
-// Rows of more than 2048 elements: one row per workgroup, split over its 4 wavefronts
-// (NC chunks per lane, 4 * NC * 1024 >= cols); the wavefront maxima meet in LDS. Against
-// one wavefront per row: [4096, 8192] 22.4 -> 20.2 us, [32760, 8192] 143.1 -> 139.9 us,
-// [32760, 4096] 72.4 -> 69.6 us, [4096, 4096] unchanged (same codes and scales).
+// Rows of more than 2048 elements: one row per workgroup, split over its WPR wavefronts
+// (NC chunks per lane, WPR * NC * 1024 >= cols); the wavefront maxima meet in LDS. Against
+// one wavefront per row, 4 wavefronts: [4096, 8192] 22.4 -> 20.2 us, [32760, 8192] 143.1 ->
+// 139.9 us, [32760, 4096] 72.4 -> 69.6 us, [4096, 4096] unchanged (same codes and scales).
+// Many rows of 4097..8192 elements take 8 wavefronts per row (one chunk per lane): at
+// [32760, 8192] 131.7 against 137.6 us, while at [4096, 8192] 4 stay ahead (18.8 against
+// 19.6 us), so 8 are used from kSplit8Rows rows on.
 constexpr int kSplitWaves = 4;
-template <int NC>
-__global__ __launch_bounds__(64 * kSplitWaves) void quant_rows_split(const uint16_t* __restrict__ x, int cols,
-                                                                    uint8_t* __restrict__ q,
-                                                                    float* __restrict__ scale) {
+constexpr int64_t kSplit8Rows = 16384;
+template <int NC, int WPR>
+__global__ __launch_bounds__(64 * WPR) void quant_rows_split(const uint16_t* __restrict__ x, int cols,
+                                                            uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
   const int part = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;  // the grid is exactly one workgroup per row
   const int nchunks = cols >> 4;
   uint4 va[NC], vb[NC];
-  qrow::load_row<NC, kSplitWaves>(x + row * cols, nchunks, lane, va, vb, part);
-  __shared__ float wave_amax[kSplitWaves];
+  qrow::load_row<NC, WPR>(x + row * cols, nchunks, lane, va, vb, part);
+  __shared__ float wave_amax[WPR];
   const float m = qrow::wave_max(qrow::lane_absmax<NC>(va, vb));
   if (lane == 0) wave_amax[part] = m;
   __syncthreads();
   float amax = wave_amax[0];
 #pragma unroll
-  for (int i = 1; i < kSplitWaves; ++i) amax = fmaxf(amax, wave_amax[i]);
-  qrow::quant_row_part<NC, kSplitWaves>(va, vb, nchunks, lane, part, amax, q + row * cols, scale + row);
+  for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, wave_amax[i]);
+  qrow::quant_row_part<NC, WPR>(va, vb, nchunks, lane, part, amax, q + row * cols, scale + row);
 }
 
 __global__ __launch_bounds__(kBlock) void quant_rows_loop(const uint16_t* __restrict__ x, int64_t rows,
@@ -81,9 +84,11 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, uint
   else if (chunks_per_lane <= 2)
     quant_rows_regs<2><<<grid, block, 0, stream>>>(x, rows, c, q, scale);
   else if (chunks_per_lane <= 4)
-    quant_rows_split<1><<<split_grid, split_block, 0, stream>>>(x, c, q, scale);
+    quant_rows_split<1, kSplitWaves><<<split_grid, split_block, 0, stream>>>(x, c, q, scale);
+  else if (chunks_per_lane <= 8 && rows >= kSplit8Rows)
+    quant_rows_split<1, 2 * kSplitWaves><<<split_grid, dim3(128 * kSplitWaves), 0, stream>>>(x, c, q, scale);
   else if (chunks_per_lane <= 8)
-    quant_rows_split<2><<<split_grid, split_block, 0, stream>>>(x, c, q, scale);
+    quant_rows_split<2, kSplitWaves><<<split_grid, split_block, 0, stream>>>(x, c, q, scale);
   else
     quant_rows_loop<<<grid, block, 0, stream>>>(x, rows, c, q, scale);
   return hipGetLastError();

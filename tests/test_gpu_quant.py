@@ -71,6 +71,18 @@ def test_edge_shapes(rows, cols):
     _check(x, f"{rows}x{cols}")
 
 
+@pytest.mark.parametrize("cols", [4112, 6160, 8192])
+def test_many_long_rows(cols):
+    # 16384 rows or more of 4097..8192 elements take eight wavefronts per row: every row
+    # against the C statement of the oracle, ragged chunk counts included
+    dev = require_gpu()
+    x = make_case(16400, 16, cols, seed=cols, kind="outlier").a
+    q, s = quant_rows(x.to(dev))
+    torch.cuda.synchronize()
+    eq, es = cref.quant_rows(bf16_bits(x))
+    assert_codes_equal(q, s, eq, es, f"16400x{cols}")
+
+
 def _bf16(values):
     return torch.tensor(np.asarray(values, np.float32)).to(torch.bfloat16)
 
