@@ -4,7 +4,7 @@ Called through the C ABI. Its output must equal fp8_linear_run's (the same kerne
 the same codes, so bit for bit), and the first output is also held to the oracle's
 linear tolerance. Two calls in a row on the shared scratch, the second with fewer
 tokens; an input above the scratch size is refused before anything runs; the e4m3fn
-kind needs no scratch.
+kind needs no scratch; the call recorded into a HIP graph and replayed on new inputs.
 """
 
 import ctypes
@@ -88,3 +88,35 @@ def test_noalloc_near_the_scratch_size():
         expect = lin(ad)
         torch.cuda.synchronize()
         assert torch.equal(out, expect)
+
+
+def test_noalloc_replayed_from_a_graph():
+    # the use the entry point exists for: recorded once into a HIP graph (no allocation
+    # inside the capture), replayed with new inputs copied in between replays; every replay
+    # must equal the eager forward on that input, bit for bit
+    dev = require_gpu()
+    case = make_case(300, 528, 1040, seed=75, kind="outlier")
+    lin = fp8.Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    a_static = torch.empty((300, 1040), dtype=torch.bfloat16, device=dev)
+    out_static = torch.empty((300, 528), dtype=torch.bfloat16, device=dev)
+    inputs = [make_case(300, 528, 1040, seed=76 + i, kind="outlier").a.to(dev) for i in range(3)]
+    a_static.copy_(inputs[0])
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):  # first call outside capture: the scratch address is looked up here
+        st = _lib.lib().fp8_linear_run_noalloc(lin._plan, 300, _p(a_static), _lib.A_BF16, None, _p(out_static),
+                                               ctypes.c_void_p(side.cuda_stream))
+        assert st == _lib.OK
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        st = _lib.lib().fp8_linear_run_noalloc(lin._plan, 300, _p(a_static), _lib.A_BF16, None, _p(out_static), cap)
+    assert st == _lib.OK
+    for x in inputs:
+        a_static.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        expect = lin(x)  # eager, with its own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, expect)
