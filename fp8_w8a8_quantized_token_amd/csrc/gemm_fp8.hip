@@ -586,7 +586,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qw) + (int64_t)n0 * K, 0,
                                         (uint32_t)rows_w * (uint32_t)K, kBufferConfig);
 
-  // epilogue operands of this thread's output (token t / 16, channel t % 16), requested now
+  // epilogue operands of this thread's output (token t / 16, channel t % 16: every output of
+  // the workgroup's tile has one thread, since TM * NW == WAVES * 64), requested now
+  static_assert(TM * kSkinnyNW == WAVES * 64, "one output per thread");
   const int et = threadIdx.x / kSkinnyNW, ec = threadIdx.x % kSkinnyNW;
   const bool evalid = et < rows_a && ec < rows_w;
   float e_sa = 0.0f, e_sw = 0.0f, e_b = 0.0f;
@@ -651,22 +653,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
 #pragma unroll
   for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
-  for (int o = threadIdx.x; o < TM * kSkinnyNW; o += WAVES * 64) {
-    const int tok = o / kSkinnyNW, ch = o % kSkinnyNW;
-    // token tok is column tok % 16 of m-tile tok / 16; channel ch is row ch of the result
-    const int src_lane = (tok & 15) + 16 * (ch >> 2);
-    float sum = 0.0f;
+  // token et is column et % 16 of m-tile et / 16; channel ec is row ec of the result
+  const int src_lane = (et & 15) + 16 * (ec >> 2);
+  float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += red[w][tok >> 4][src_lane][ch & 3];
-    if (tok < rows_a && ch < rows_w) {
-      const float sa = o == (int)threadIdx.x ? e_sa : args.a_scale[m0 + tok];
-      const float sw = o == (int)threadIdx.x ? e_sw : args.w_scale[n0 + ch];
-      const float b = o == (int)threadIdx.x ? e_b : (args.bias ? __uint_as_float((uint32_t)args.bias[n0 + ch] << 16) : 0.0f);
-      const float v = __builtin_fmaf(sum * sa, sw, b);
-      args.out[(int64_t)(m0 + tok) * args.n + n0 + ch] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
-    }
+  for (int w = 0; w < WAVES; ++w) sum += red[w][et >> 4][src_lane][ec & 3];
+  if (evalid) {
+    const float v = __builtin_fmaf(sum * e_sa, e_sw, e_b);
+    args.out[(int64_t)(m0 + et) * args.n + n0 + ec] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
   }
-  (void)evalid;
 }
 
 template <int MT>
