@@ -231,3 +231,11 @@ def test_tensor_quant_validation(lib):
     assert d(A, 20, 0, A, A, None) == _lib.ERR_BAD_SHAPE
     assert d(A, 16, 0, A, MIS16, None) == _lib.ERR_MISALIGNED
     assert d(A, 0, 0, A, A, None) == _lib.OK
+
+
+def test_noalloc_run_validation(lib):
+    # checks that need no plan and no device: every call below returns before any HIP call
+    A = ALIGNED
+    assert _lib.NOALLOC_SCRATCH_BYTES == 80 << 20
+    assert lib.fp8_linear_run_noalloc(None, 4, A, _lib.A_BF16, None, A, None) == _lib.ERR_INVALID_ARG
+    assert lib.fp8_linear_run_noalloc(None, 4, A, _lib.A_E4M3, A, A, None) == _lib.ERR_INVALID_ARG
