@@ -231,7 +231,10 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
  * fp8_linear_run's. The scratch keeps the last call's codes; every BF16 run rewrites
  * all the codes and scales its GEMM reads, so nothing needs clearing. All calls on
  * one GPU share its scratch: two BF16 runs that overlap in time on the same GPU (for
- * example on two streams) race, and the caller must order them.
+ * example on two streams) race, and the caller must order them. The scratch's address is
+ * looked up (hipGetSymbolAddress) at the first BF16 call with m > 0 on each GPU; a caller
+ * that records the call into a HIP graph makes one such call outside the capture first
+ * (a lookup refused during capture returns FP8W8A8_ERR_HIP and launches nothing).
  */
 #define FP8W8A8_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
 int fp8_linear_run_noalloc(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind,
