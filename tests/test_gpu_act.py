@@ -118,16 +118,17 @@ def test_fused_equals_unfused_on_gpu(dev, tables, kind, rows, cols):
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
-@pytest.mark.parametrize("rows", [4096, 32760])
-def test_fused_producer_full_size_ffn_down_input(dev, tables, rows):
-    # the FFN-down input at the FFN shape [4096, 8192] and at the DiT-block size [32760, 8192],
-    # every row: the oracle's exact activation table, then the C statement of the per-token
-    # quantiser (pinned bit for bit to oracle.quant)
+@pytest.mark.parametrize("kind,rows", [("gelu_tanh", 4096), ("gelu_tanh", 32760), ("gelu_erf", 4096),
+                                       ("silu", 4096)])
+def test_fused_producer_full_size_ffn_down_input(dev, tables, kind, rows):
+    # the FFN-down input at the FFN shape [4096, 8192] (every activation) and at the DiT-block
+    # size [32760, 8192], every row: the oracle's exact activation table, then the C statement
+    # of the per-token quantiser (pinned bit for bit to oracle.quant)
     x = _normal(rows, 8192, seed=21)
-    q, s = fp8.act_quant_rows(x.to(dev), tables["gelu_tanh"])
+    q, s = fp8.act_quant_rows(x.to(dev), tables[kind])
     torch.cuda.synchronize()
-    eq, es = cref.quant_rows(oact.act_bf16_bits(bf16_bits(x), "gelu_tanh"))
-    assert_codes_equal(q, s, eq, es, f"gelu_tanh producer [{rows}, 8192]")
+    eq, es = cref.quant_rows(oact.act_bf16_bits(bf16_bits(x), kind))
+    assert_codes_equal(q, s, eq, es, f"{kind} producer [{rows}, 8192]")
 
 
 def test_fused_producer_feeds_the_fp8_linear(dev, tables):

@@ -198,6 +198,20 @@ def test_qkv_shared_quantisation_full_size():
                           oracle_weight=wq)
 
 
+@pytest.mark.parametrize("m", [1, 26, 32])
+@pytest.mark.parametrize("config", ["ffn_up", "ffn_down"])
+def test_few_tokens_through_the_ffn_weights(config, m):
+    # a few tokens (the skinny weight stream, configuration 5) against the full FFN weights,
+    # bf16 input: every code and every output element against the oracle
+    dev = require_gpu()
+    cfg = make_config(config)
+    layer, act = cfg["layers"][0]
+    w, b = cfg["weights"][layer], cfg["biases"][layer]
+    lin = Fp8Linear(w.to(dev), b.to(dev))
+    assert lin.config(m)[0] == 5
+    _full_size_linear(cfg["activations"][act][:m].contiguous(), w, b, dev, f"{config} m={m}", lin=lin)
+
+
 @pytest.fixture(scope="module")
 def dit_block():
     """The DiT-block config, each activation quantised once on the GPU (codes checked
