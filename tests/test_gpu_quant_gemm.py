@@ -107,6 +107,13 @@ def test_ffn_up_full_size(dev):
     _check(case, dev, label="FFN-up")
 
 
+@pytest.mark.slow
+def test_ffn_down_full_size(dev):
+    # rows of 8192 in the shares (eight register chunks per lane), 16 tiles of k = 8192
+    case = make_case(4096, 2048, 8192, seed=42, kind="gelu")
+    _check(case, dev, label="FFN-down")
+
+
 def test_refused_under_graph_capture(dev):
     # the launch's generation number is chosen on the host per call; a graph would replay
     # it, so a call on a capturing stream is refused and nothing is recorded

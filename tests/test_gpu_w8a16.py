@@ -145,6 +145,26 @@ def test_ffn_full_size(name):
     assert_linear_close_rows(out, lambda r0, r1: ow.w8a16_ref(a_bits[r0:r1], qw, sw, b_bits), f"w8a16 {name}")
 
 
+@pytest.mark.slow
+def test_ffn_up_full_size_per_tensor_e5m2():
+    # the state-dict converter's e5m2 weight (one scale for the tensor) at the FFN-up shape:
+    # the codes and the scale bit for bit, every output element against the oracle
+    dev = require_gpu()
+    cfg = make_config("ffn_up")
+    a, w, b = cfg["activations"]["a"], cfg["weights"]["ffn_up"], cfg["biases"]["ffn_up"]
+    q, s = fp8.quant_tensor(w.to(dev), "e5m2")
+    lin = fp8.Fp8WeightOnlyLinear(w_fp8=q, w_scale=s, bias=b.to(dev), fmt="e5m2")
+    out = lin(a.to(dev))
+    torch.cuda.synchronize()
+    eq, es = otq.quant_tensor(bf16_bits(w), "e5m2")
+    assert np.array_equal(q.cpu().numpy(), eq)
+    assert s.cpu().numpy().view(np.uint32)[0] == np.float32(es).view(np.uint32)
+    sw = np.full(w.shape[0], es, np.float32)
+    a_bits, b_bits = bf16_bits(a), bf16_bits(b)
+    assert_linear_close_rows(out, lambda r0, r1: ow.w8a16_ref(a_bits[r0:r1], eq, sw, b_bits, fmt="e5m2"),
+                             "w8a16 ffn_up per-tensor e5m2")
+
+
 @pytest.mark.gpu
 def test_w8a16_selector_picks_the_measured_best():
     # timed on MI355X (every configuration interleaved in one process): 256 x 256 at FFN-up,
