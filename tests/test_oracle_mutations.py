@@ -255,6 +255,15 @@ def test_e5m2_half_up_is_caught(monkeypatch):
     _fails(t5.test_encode_matches_brute_force_at_every_boundary)
 
 
+def test_e5m2_missing_saturation_is_caught(monkeypatch):
+    # without the clamp a quotient of 65536 (the smallest bf16 amax over its rounded-down
+    # subnormal scale) would encode as 0x7C, the infinity code
+    real = e5m2_mod.encode
+    monkeypatch.setattr(e5m2_mod, "E5M2_MAX", np.inf)
+    assert real(np.array([65536.0], np.float32))[0] == 0x7C
+    _fails(ttq.test_worked_subnormal_scale_saturates_e5m2)
+
+
 def test_per_row_scale_in_the_tensor_quantiser_is_caught(monkeypatch):
     def per_row(x_bits, fmt):
         q, s = quant_mod.quant_rows(np.atleast_2d(np.asarray(x_bits, np.uint16)))
