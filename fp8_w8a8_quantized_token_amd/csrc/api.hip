@@ -159,6 +159,7 @@ struct Family {
   TileModel (*model)(int);
   int skinny;           // configuration for m <= skinny_max_m (outside the tile model), or -1
   int64_t skinny_max_m;
+  int persistent;       // persistent form of configuration 0 (outside the tile model), or -1
 };
 // m buckets: rows <= bound[b] use the configuration chosen at that bound; the last bucket
 // is unbounded and chosen at 32768 rows. The W8A8 model picks the measured best on all 17
@@ -176,10 +177,19 @@ static_assert(sizeof(kW8A16Bounds) / sizeof(int64_t) <= kMaxBuckets, "bucket cou
 // 4.0 against 9.0. Above 32 tokens it loads the weight once per 32 tokens and loses at
 // wide n (m = 64, n = 8192: 14.8 against 9.6 us), so it serves m <= 32 only.
 constexpr int kW8A8Skinny = 5;
+// The persistent form of the 256 x 256 tiles (one workgroup per CU walking its tiles, the
+// next tile's first stages requested before the current tile's epilogue) is output-for-
+// output identical to configuration 0. Timed against it on 32 shapes (m 2048 .. 32760,
+// n 2048 / 8192, k 1024 .. 8192, interleaved in one process) it was faster wherever each
+// CU had two or more tiles and k was 2048 or 4096 (FFN-up 69.3 -> 67.4 us, 8192 x 8192 x
+// 2048 122.8 -> 119.8, 32760 x 8192 x 2048 474 -> 465), within +-1% or slower elsewhere:
+// its fill offsets cost a little per k step, so with one tile per CU, or at k = 8192, the
+// saved prologue does not pay for them, and at k = 1024 the results went either way.
+constexpr int kW8A8Persistent = 6;
 const Family kW8A8{kW8A8Bounds, (int)(sizeof(kW8A8Bounds) / sizeof(int64_t)), gemm_config_count, gemm_config,
-                   gemm_workgroups, gemm_threads, w8a8_tile_model, kW8A8Skinny, 32};
+                   gemm_workgroups, gemm_threads, w8a8_tile_model, kW8A8Skinny, 32, kW8A8Persistent};
 const Family kW8A16{kW8A16Bounds, (int)(sizeof(kW8A16Bounds) / sizeof(int64_t)), w8a16_config_count, w8a16_config,
-                    w8a16_workgroups, w8a16_threads, w8a16_tile_model, -1, 0};
+                    w8a16_workgroups, w8a16_threads, w8a16_tile_model, -1, 0, -1};
 
 bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
   return f.workgroups(config, m, n) * f.threads(config) < kMaxGridThreads;
@@ -204,14 +214,18 @@ int choose_config(const Family& f, int64_t m, int64_t n, int64_t k, int cus) {
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < f.count(); ++c) {
-    if (c == f.skinny || !grid_fits(f, c, m, n)) continue;
+    if (c == f.skinny || c == f.persistent || !grid_fits(f, c, m, n)) continue;
     const double t = model_time(f, c, m, n, k, cus);
     if (best < 0 || t < best_t) {
       best = c;
       best_t = t;
     }
   }
-  return best < 0 ? 0 : best;
+  if (best < 0) best = 0;
+  if (best == 0 && f.persistent >= 0 && k >= 2048 && k <= 4096 && f.workgroups(0, m, n) >= 2 * (int64_t)cus &&
+      grid_fits(f, f.persistent, m, n))
+    best = f.persistent;
+  return best;
 }
 
 
@@ -449,7 +463,7 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
     sa = ws_scale;
   }
   hipError_t e = launch_gemm(config, m, plan->n, plan->k, qa, sa, plan->w, plan->w_scale, plan->bias,
-                             static_cast<uint16_t*>(out_bf16), s);
+                             static_cast<uint16_t*>(out_bf16), plan->cu_count, s);
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 
@@ -513,11 +527,13 @@ int fp8_gemm_run_config(int config_id, int64_t m, int64_t n, int64_t k, const vo
   if (!aligned(qa, 16) || !aligned(out_bf16, 16) || !aligned(a_scale, 4)) return FP8W8A8_ERR_MISALIGNED;
   if (m == 0) return FP8W8A8_OK;
   if (!grid_fits(config_id, m, n)) return FP8W8A8_ERR_BAD_SHAPE;
-  st = current_device_ok();
+  int cus = 0;
+  st = current_device_ok(&cus);
   if (st != FP8W8A8_OK) return st;
   hipError_t e = launch_gemm(config_id, m, n, k, static_cast<const uint8_t*>(qa), a_scale,
                              static_cast<const uint8_t*>(w_fp8), w_scale, static_cast<const uint16_t*>(bias_bf16),
-                             static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(stream));
+                             static_cast<uint16_t*>(out_bf16), cus > 0 ? cus : 256,
+                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 

@@ -65,16 +65,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // is not read again by this kernel, and marking its lines for early eviction keeps the
 // operand panels other tiles still read in the XCD's L2 (FFN-up 68.5 -> 66.1 us,
 // 32760 x 2048 x 2048 138.3 -> 129.5 us, bit-identical output).
-template <int WTM, int RC>
+// ALWAYS_ISSUE: a piece wholly past m still issues its stores (an empty descriptor drops
+// them), so a caller that counts its outstanding memory operations knows the number.
+template <int WTM, int RC, bool ALWAYS_ISSUE = false>
 __device__ __forceinline__ void store_wave_tile(const uint8_t* wout, int lane, uint16_t* out, int m, int n,
                                                 int row0, int col0) {
   constexpr int kRowsPerStore = 64 / RC;
   static_assert(64 % RC == 0 && WTM % kRowsPerStore == 0, "row segments tile the wavefront");
-  const int rows_valid = min(WTM, m - row0);
-  if (rows_valid <= 0) return;
+  const int rows_valid = max(0, min(WTM, m - row0));
+  if (!ALWAYS_ISSUE && rows_valid == 0) return;
   const uint32_t row_bytes = (uint32_t)n * 2u;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      out + (int64_t)row0 * n, 0, (uint32_t)rows_valid * row_bytes, kBufferConfig);
+  // base and size are uniform; readfirstlane keeps the descriptor in SGPRs even where the
+  // compiler cannot tell (no waterfall loop around the stores)
+  const uint64_t base = reinterpret_cast<uint64_t>(out + (int64_t)row0 * n);
+  const uint64_t ubase = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base) |
+                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)) << 32);
+  const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)rows_valid * row_bytes));
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ubase), 0, nrec, kBufferConfig);
   const int c = lane % RC;
   const int ncol = col0 + c * 8;
   const uint32_t voff = ncol < n ? (uint32_t)(lane / RC) * row_bytes + (uint32_t)ncol * 2u : kOutOfRange;
@@ -91,10 +99,10 @@ __device__ __forceinline__ void store_wave_tile(const uint8_t* wout, int lane, u
 // Workgroup id -> (tile_m, tile_n). Hardware deals ids to XCDs round-robin (id % 8);
 // renumber so XCD x owns a contiguous range of logical tiles, then walk that range in
 // groups of GROUP_M tile rows so concurrent tiles share operand panels in L2.
+// tile_coords_at: the same for logical tile `id` of `nwg` (a persistent workgroup's id plus
+// a multiple of its grid, which keeps id % 8 its own XCD when the grid is a multiple of 8).
 template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = gridDim.x;
-  const int id = blockIdx.x;
+__device__ __forceinline__ void tile_coords_at(int id, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int q = nwg / kXcds, r = nwg % kXcds;
   const int xcd = id % kXcds, local = id / kXcds;
   const int logical = xcd * q + min(xcd, r) + local;
@@ -105,6 +113,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int in_group = logical - group * group_size;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
+}
+
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  tile_coords_at<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
 }
 
 // Distinct LDS objects per (kernel, stage).

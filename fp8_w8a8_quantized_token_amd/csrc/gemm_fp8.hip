@@ -48,6 +48,10 @@
 //   * A skinny form for a few dozen tokens (the 26-row encoder input of the QKV
 //     projections): a weight stream over many workgroups with k split across waves and
 //     operands loaded straight into registers (gemm_fp8_skinny below).
+//   * A persistent form of the 256 x 256 tiles (PERSIST): one workgroup per CU walks
+//     its tiles and requests the next tile's first two stages as soon as the current
+//     tile's k loop is done, so they land during its epilogue instead of after it. It
+//     computes exactly what configuration 0 computes, in the same order.
 #include <algorithm>
 
 #include "internal.h"
@@ -74,6 +78,34 @@ struct GemmArgs {
   unsigned long long epoch;
   int shares, rows_per_share;
 };
+
+// The kernel's arguments read afresh from the kernel-argument segment. The address goes
+// through an empty asm, so the compiler cannot reuse the values it loaded at the start:
+// a persistent workgroup that needs them again only after its k loop does not hold them
+// in scalar registers through it.
+typedef const __attribute__((address_space(4))) GemmArgs* KernargGemmArgs;
+__device__ __forceinline__ GemmArgs reload_args() {
+  uint64_t p = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  // (the compiler takes an asm result as divergent; the address is uniform)
+  p = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+  const KernargGemmArgs k = reinterpret_cast<KernargGemmArgs>(p);
+  GemmArgs r{};
+  r.qa = k->qa;
+  r.a_scale = k->a_scale;
+  r.qw = k->qw;
+  r.w_scale = k->w_scale;
+  r.bias = k->bias;
+  r.out = k->out;
+  r.m = k->m;
+  r.n = k->n;
+  r.k = k->k;
+  r.tiles_m = k->tiles_m;
+  r.tiles_n = k->tiles_n;
+  r.shares = k->shares;
+  return r;
+}
 
 constexpr int kScDevice = 16;  // cache-policy bit sc1: device-scope coherent access
 constexpr uint64_t kStealAfterTicks = 10000;  // 100 us of the 100 MHz real-time clock
@@ -176,16 +208,26 @@ __device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int
   __syncthreads();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED, bool PERSIST>
 struct KernelTag {};
 
 // FUSED: the single-launch form. The activation codes and scales do not exist yet at
 // launch: the first `shares` workgroups quantise the bf16 activation into them
 // (quant_share), every workgroup waits for the shares of its tile's tokens (await_shares), and the weight
 // half of the first stages is requested before all that so it lands meanwhile.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false>
+//
+// PERSIST: one workgroup per CU walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... . Once
+// a tile's k loop has passed its last barrier the stage ring is free, so the next tile's
+// first two stages are requested right then and land while this tile's epilogue runs.
+// The epilogue therefore cannot stage its output in the ring: it goes through a region
+// of its own (4 KiB per wave, which also holds the tile's epilogue operands between
+// tiles), 32 token rows per wave at a time, and issues exactly kEpiStores stores per
+// wave, so that the wait for the next tile's stages (older than the stores) is an exact
+// count.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false,
+          bool PERSIST = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
-  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED>;
+  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED, PERSIST>;
   static_assert(BK == 64 || BK == 128, "stage depth in k bytes");
   constexpr int H = BK / 64;         // 32x32x64 MFMA k-steps per stage
   constexpr int CPR = BK / 16;       // 16-byte chunks per tile row
@@ -201,7 +243,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(kRowGroups % kWaves == 0, "fill work must split evenly across waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
   constexpr int kEpiBytes = (BM + 2 * BN) * 4;  // the tile's a_scale, w_scale, bias (fp32)
-  static_assert(STAGES * kStageBytes + kEpiBytes <= 160 * 1024, "LDS budget of a CU");
+  // PERSIST's output staging: 32 token rows of the wave tile per wave; the epilogue
+  // operands share the region (they are in registers while it holds output)
+  constexpr int kPieceRows = 32;
+  constexpr int kPieceBytes = kPieceRows * (BN / WAVES_N) * 2;
+  constexpr int kStagingBytes = PERSIST ? kWaves * kPieceBytes : 0;
+  static_assert(!PERSIST || kEpiBytes <= kStagingBytes, "epilogue operands fit in the staging region");
+  static_assert(STAGES * kStageBytes + (PERSIST ? kStagingBytes : kEpiBytes) <= 160 * 1024, "LDS budget of a CU");
   // Which waves issue the DMA fills. A burst of fills stalls the issuing wave at issue
   // while the texture path drains them, and the matrix core idles if both waves of a
   // SIMD stall together. With 8 waves (two per SIMD) only waves 0..3, one per SIMD,
@@ -218,6 +266,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   constexpr bool kSplitRefill = STAGES == 2 && H == 2 && kFillWaves < kWaves;
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
   static_assert(!FUSED || STAGES == 2, "the single-launch prologue's fill order assumes two stages");
+  static_assert(!PERSIST || (!FUSED && STAGES == 2 && kWaves == 8),
+                "the persistent form hands the two-stage ring of the 8-wave tile to the next tile");
 
   auto buf = [](int s) -> uint8_t* {
     switch (s) {
@@ -231,23 +281,29 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   };
 
   const int lane = threadIdx.x & 63;
+  const int ntiles = args.tiles_m * args.tiles_n;
+  int vtile = blockIdx.x;  // PERSIST: the logical tile this workgroup works on
   int tm, tn;
-  tile_coords<GROUP_M>(args.tiles_m, args.tiles_n, tm, tn);
+  if constexpr (PERSIST) tile_coords_at<GROUP_M>(vtile, ntiles, args.tiles_m, args.tiles_n, tm, tn);
+  else tile_coords<GROUP_M>(args.tiles_m, args.tiles_n, tm, tn);
   tm = __builtin_amdgcn_readfirstlane(tm);  // uniform by construction; keep it in SGPRs
   tn = __builtin_amdgcn_readfirstlane(tn);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  const int m0 = tm * BM, n0 = tn * BN;
+  int m0 = tm * BM, n0 = tn * BN;
   const int K = args.k;
-  const int rows_a = min(BM, args.m - m0);
-  const int rows_w = min(BN, args.n - n0);
-  const v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
-  const v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  int rows_a = min(BM, args.m - m0);
+  int rows_w = min(BN, args.n - n0);
+  v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+  v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
   // Epilogue operands of this tile, one value per thread, requested now; they arrive
   // with the first stage and are parked in LDS, so they hold no registers during the
   // k loop.
-  float* const epi_sa = reinterpret_cast<float*>(stage_buf<Tag, 7, kEpiBytes>());
+  uint8_t* epi_base;
+  if constexpr (PERSIST) epi_base = stage_buf<Tag, 8, kStagingBytes>();
+  else epi_base = stage_buf<Tag, 7, kEpiBytes>();
+  float* const epi_sa = reinterpret_cast<float*>(epi_base);
   float* const epi_sw = epi_sa + BM;
   float* const epi_b = epi_sw + BN;
   const int tid = threadIdx.x;
@@ -269,8 +325,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   const int fr = lane / CPR;
   const int fchunk0_ = (lane % CPR) ^ swz<BK>(fr);            // row group with g * RPF % 16 == 0
   const int fchunk1_ = (lane % CPR) ^ swz<BK>(fr + RPF % 16);  // row group with g * RPF % 16 == 8
-  const uint32_t foff0_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0_;
-  const uint32_t foff1_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1_;
+  // (PERSIST passes these, and the wave index and k the fills use, through an empty asm
+  // at each tile so the compiler does not keep the per-fill offsets and LDS addresses
+  // derived from them alive across the epilogue)
+  uint32_t foff0_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk0_;
+  uint32_t foff1_ = (uint32_t)fr * (uint32_t)K + 16u * (uint32_t)fchunk1_;
+  int fwave = wave, fK = K;  // the fills' copies (same laundering)
 
   // part: 0 = the whole stage, 1 = activation rows only, 2 = weight rows only
   auto issue = [&](uint8_t* base, int k0, int part = 0) {
@@ -288,21 +348,46 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       foff0 = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)fchunk0;
       foff1 = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)fchunk1;
     }
-    const bool kvalid0 = k0 + 16 * fchunk0 < K;
-    const bool kvalid1 = k0 + 16 * fchunk1 < K;
+    const bool kvalid0 = k0 + 16 * fchunk0 < fK;
+    const bool kvalid1 = k0 + 16 * fchunk1 < fK;
+    if constexpr (PERSIST) {
+      // Every fill of this wave has the same row parity (its row groups step by
+      // kFillWaves * RPF rows, a multiple of 16) and the activation and weight halves
+      // start at the same row offset, so one base per stage plus a multiple of a scalar
+      // stride gives every fill's offset: one register, where one per fill held through
+      // the k loop leaves the loop short of registers once it sits inside the tile loop.
+      static_assert((kFillWaves * RPF) % 16 == 0 && FA * kFillWaves * RPF == BM, "one offset chain");
+      const bool odd = ((fwave * RPF) & 15) != 0;
+      const bool kvalid = odd ? kvalid1 : kvalid0;
+      const uint32_t v0 = (uint32_t)(fwave * RPF) * (uint32_t)fK + (odd ? foff1 : foff0) + (uint32_t)k0;
+      uint32_t stride = (uint32_t)(kFillWaves * RPF) * (uint32_t)fK;
+      asm volatile("" : "+s"(stride));
+      stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)stride);
+      // (the compiler forms v0 + j * stride as one 64-bit multiply-add per fill; every
+      // formulation with plain adds measured here tipped the loop into spilling)
+#pragma unroll
+      for (int j = 0; j < F; ++j) {
+        if ((part == 1 && j >= FA) || (part == 2 && j < FA)) continue;
+        const int g = fwave + j * kFillWaves;
+        const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
+        const uint32_t vo = v0 + (uint32_t)(j < FA ? j : j - FA) * stride;
+        dma16(j < FA ? rsrc_a : rsrc_w, dst, kvalid ? vo : kOutOfRange);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       if ((part == 1 && j >= FA) || (part == 2 && j < FA)) continue;
-      const int g = wave + j * kFillWaves;
+      const int g = fwave + j * kFillWaves;
       const bool odd = ((g * RPF) & 15) != 0;
       const bool kvalid = odd ? kvalid1 : kvalid0;
       const uint32_t foff = odd ? foff1 : foff0;
       const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
       if (j < FA) {
-        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)fK + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_a, dst, vo);
       } else {
-        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)fK + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_w, dst, vo);
       }
     }
@@ -317,20 +402,20 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(!kPrologueAll || (kRowGroups % kWaves == 0 && (BM / RPF) % kWaves == 0),
                 "prologue fills split evenly");
   auto issue_all = [&](uint8_t* base, int k0) {
-    const bool kvalid0 = k0 + 16 * fchunk0_ < K;
-    const bool kvalid1 = k0 + 16 * fchunk1_ < K;
+    const bool kvalid0 = k0 + 16 * fchunk0_ < fK;
+    const bool kvalid1 = k0 + 16 * fchunk1_ < fK;
 #pragma unroll
     for (int j = 0; j < FW; ++j) {
-      const int g = wave + j * kWaves;
+      const int g = fwave + j * kWaves;
       const bool odd = ((g * RPF) & 15) != 0;
       const bool kvalid = odd ? kvalid1 : kvalid0;
       const uint32_t foff = odd ? foff1_ : foff0_;
       const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
       if (j < FAW) {
-        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF) * (uint32_t)fK + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_a, dst, vo);
       } else {
-        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)K + foff + (uint32_t)k0 : kOutOfRange;
+        const uint32_t vo = kvalid ? (uint32_t)(g * RPF - BM) * (uint32_t)fK + foff + (uint32_t)k0 : kOutOfRange;
         dma16(rsrc_w, dst, vo);
       }
     }
@@ -418,7 +503,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue_all(buf(s), s * BK);
-    wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
+    // PERSIST waits for both first stages here, as it does for every later tile
+    if constexpr (PERSIST) wait_vm_lgkm0<0>();
+    else wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
   } else {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
@@ -433,7 +520,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     epi_b[tid] = pre_b;
   }
   block_barrier();
-  read_frags(buf(0), 0, f0);
 
   auto sub = [&](int u, int s, int h, Frags& cur, Frags& nxt) {
     // s = stage index of u modulo STAGES, h = half of u (compile-time after unrolling)
@@ -441,9 +527,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     if (h == H - 1) {
       if (t + 1 < nst) {
         // stage t + 1 complete: the first stages came from every wave (FW each), later
-        // ones from the filling waves (F each)
-        if (kPrologueAll && t == 0) wait_stage<FW, STAGES>(min(nst - 2, STAGES - 2));
+        // ones from the filling waves (F each). PERSIST: both first stages were waited
+        // for before the loop, and the previous tile's output stores may still be in
+        // flight; a wave that issues no refills has nothing else outstanding.
+        if (PERSIST && t == 0) wait_vm_lgkm0<63>();
+        else if (kPrologueAll && t == 0) wait_stage<FW, STAGES>(min(nst - 2, STAGES - 2));
         else if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
+        else if (PERSIST) wait_vm_lgkm0<63>();
         else wait_vm_lgkm0<0>();
         block_barrier();
         if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK, kSplitRefill ? 1 : 0);
@@ -458,6 +548,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     interleave_mfma_ds_read<FM * FN, 2 * (FM + FN)>();
   };
   constexpr int kUnroll = 2 * STAGES * H;  // whole stage ring, even number of sub-steps
+  for (;;) {  // one pass per tile (PERSIST), else exactly one
+  if constexpr (PERSIST) {
+    asm volatile("" : "+v"(foff0_), "+v"(foff1_), "+s"(fwave), "+s"(fK));
+    fwave = __builtin_amdgcn_readfirstlane(fwave);
+    fK = __builtin_amdgcn_readfirstlane(fK);
+  }
+  read_frags(buf(0), 0, f0);
   for (int u0 = 0; u0 < nsub; u0 += kUnroll) {
 #pragma unroll
     for (int v = 0; v < kUnroll; v += 2) {
@@ -480,21 +577,26 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(kWavesPerBuf >= 1 && (kWaves + kWavesPerBuf - 1) / kWavesPerBuf <= STAGES,
                 "output staging fits in the stage buffers");
   static_assert(64 % RC == 0 && (WTM * RC) % 64 == 0, "row segments tile the wavefront");
+  // (PERSIST: the lane id goes through an empty asm so that the epilogue's per-lane
+  // addresses are formed here, not hoisted above the k loop and held through it)
+  int elane = lane;
+  if constexpr (PERSIST) asm volatile("" : "+v"(elane));
   float r_sa[FM];
   float4 r_sw[FN][4], r_b[FN][4];
 #pragma unroll
-  for (int j = 0; j < FM; ++j) r_sa[j] = epi_sa[wm * WTM + j * 32 + (lane & 31)];
+  for (int j = 0; j < FM; ++j) r_sa[j] = epi_sa[wm * WTM + j * 32 + (elane & 31)];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int nl = wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
+      const int nl = wn * WTN + i * 32 + 8 * q + 4 * (elane >> 5);
       r_sw[i][q] = *reinterpret_cast<const float4*>(epi_sw + nl);
       r_b[i][q] = *reinterpret_cast<const float4*>(epi_b + nl);
     }
   wait_vm_lgkm0<63>();
   block_barrier();
 
+  if constexpr (!PERSIST) {
   uint8_t* wout = buf(wave / kWavesPerBuf) + (wave % kWavesPerBuf) * kWaveOutBytes;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -520,15 +622,107 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   }
   // own region only: LDS executes one wave's accesses in order, no barrier needed
   store_wave_tile<WTM, RC>(wout, lane, args.out, args.m, args.n, m0 + wm * WTM, n0 + wn * WTN);
+  break;
+  } else {
+    // Every wave has read the ring and this tile's epilogue operands (barrier above).
+    // (args.shares holds the persistent grid size)
+    const GemmArgs ra = reload_args();
+    const int er0 = m0 + wm * WTM, ec0 = n0 + wn * WTN;
+    const int nt = ra.tiles_m * ra.tiles_n;
+    vtile += ra.shares;
+    const bool more = vtile < nt;
+    pre_sa = 0.0f;  // (set on every path: no value carried round the tile loop)
+    pre_sw = 0.0f;
+    pre_b = 0.0f;
+    if (more) {
+      tile_coords_at<GROUP_M>(vtile, nt, ra.tiles_m, ra.tiles_n, tm, tn);
+      tm = __builtin_amdgcn_readfirstlane(tm);
+      tn = __builtin_amdgcn_readfirstlane(tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rows_a = min(BM, ra.m - m0);
+      rows_w = min(BN, ra.n - n0);
+      rsrc_a = make_rsrc(ra.qa + (int64_t)m0 * ra.k, (uint32_t)rows_a * (uint32_t)ra.k);
+      rsrc_w = make_rsrc(ra.qw + (int64_t)n0 * ra.k, (uint32_t)rows_w * (uint32_t)ra.k);
+      if (tid < BM && tid < rows_a) pre_sa = ra.a_scale[m0 + tid];
+      if (tid < BN && tid < rows_w) {
+        pre_sw = ra.w_scale[n0 + tid];
+        if (ra.bias) pre_b = __uint_as_float((uint32_t)ra.bias[n0 + tid] << 16);
+      }
+      asm volatile("" : "+v"(foff0_), "+v"(foff1_), "+s"(fwave), "+s"(fK));
+      fwave = __builtin_amdgcn_readfirstlane(fwave);
+      fK = __builtin_amdgcn_readfirstlane(fK);
+#pragma unroll
+      for (int st = 0; st < STAGES; ++st)
+        if (st < nst) issue_all(buf(st), st * BK);
+    }
+    // Output in pieces of 32 token rows (MFMA fragment j): the wave writes its values
+    // to its piece (chunk c of row r at position c ^ (r % RC)), which goes out as whole
+    // 128-byte lines. LDS executes one wave's accesses in order, so the next piece may
+    // overwrite the region right after the previous one's reads.
+    constexpr int kEpiStores = FM * (kPieceRows / (64 / RC));
+    static_assert(kPieceRows == 32 && kPieceBytes == kPieceRows * RC * 16, "piece geometry");
+    uint8_t* const piece = epi_base + wave * kPieceBytes;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int r = elane & 31;
+      const float sa = r_sa[j];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c8 = i * 32 + 8 * q + 4 * (elane >> 5);
+          const float4 sw4 = r_sw[i][q];
+          const float4 b4 = r_b[i][q];
+          const v16f& a = acc[i][j];
+          const float o0 = __builtin_fmaf(a[4 * q + 0] * sa, sw4.x, b4.x);
+          const float o1 = __builtin_fmaf(a[4 * q + 1] * sa, sw4.y, b4.y);
+          const float o2 = __builtin_fmaf(a[4 * q + 2] * sa, sw4.z, b4.z);
+          const float o3 = __builtin_fmaf(a[4 * q + 3] * sa, sw4.w, b4.w);
+          const int chunk = c8 >> 3, half = (c8 >> 2) & 1;
+          *reinterpret_cast<uint2*>(piece + r * (RC * 16) + ((chunk ^ (r % RC)) << 4) + (half << 3)) =
+              make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        }
+      store_wave_tile<kPieceRows, RC, true>(piece, elane, ra.out, ra.m, ra.n, er0 + j * 32, ec0);
+    }
+    if (!more) break;
+    // the next tile's fills and epilogue operands are older than this wave's kEpiStores
+    // stores; every wave has read its last piece before the operands overwrite the region
+    static_assert(kEpiStores < 64, "vmcnt range");
+    wait_vm_lgkm0<kEpiStores>();
+    block_barrier();
+    if (tid < BM) epi_sa[tid] = pre_sa;
+    if (tid < BN) {
+      epi_sw[tid] = pre_sw;
+      epi_b[tid] = pre_b;
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    block_barrier();
+  }
+  }
 }
 
-template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false>
-hipError_t launch(const GemmArgs& a, hipStream_t stream) {
+// PERSIST: one workgroup per CU (the LDS of a 256 x 256 tile admits no second), the
+// count rounded down to a multiple of the XCD count so that each workgroup's later tiles
+// stay on its own XCD; never more workgroups than tiles.
+template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false, bool PERSIST = false>
+hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
-  const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED><<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+  const int64_t tiles = (int64_t)args.tiles_m * args.tiles_n;
+  int64_t wgs = tiles;
+  if (PERSIST) {
+    wgs = std::min<int64_t>(tiles, cus >= kXcds ? (int64_t)(cus / kXcds) * kXcds : std::max(cus, 1));
+    args.shares = (int)wgs;  // the persistent form's stride over the tiles
+  }
+  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED, PERSIST>
+      <<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -682,6 +876,7 @@ const GemmConfig kConfigs[] = {
     {3, 128, 128, 4, 2, "bm128_bn128_w2x2_s2"},
     {4, 64, 64, 4, 3, "bm64_bn64_w2x2_s3"},
     {5, 32, 16, 8, 0, "skinny_m32_n16_w8"},
+    {6, 256, 256, 8, 2, "bm256_bn256_w2x4_s2_persistent"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -703,7 +898,7 @@ int gemm_threads(int id) {
 }
 
 hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* qa, const float* a_scale,
-                       const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
+                       const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out, int cus,
                        hipStream_t stream) {
   GemmArgs a{qa, a_scale, qw, w_scale, bias, out, (int)m, (int)n, (int)k, 0, 0};
   switch (id) {
@@ -713,6 +908,7 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 3: return launch<128, 128, 2, 2, 2, 128, 8>(a, stream);
     case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
     case 5: return launch_skinny<2>(a, stream);
+    case 6: return launch<256, 256, 2, 4, 2, 128, 4, false, true>(a, stream, cus);
     default: return hipErrorInvalidValue;
   }
 }

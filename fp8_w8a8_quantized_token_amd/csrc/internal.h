@@ -49,9 +49,10 @@ const GemmConfig* gemm_config(int id);
 int64_t gemm_workgroups(int id, int64_t m, int64_t n);
 int gemm_threads(int id);
 
-// Launch configuration `id` for out[m, n] = epilogue(qa[m, k] x qw[n, k]^T).
+// Launch configuration `id` for out[m, n] = epilogue(qa[m, k] x qw[n, k]^T). cus: the
+// device's compute units (sizes the grid of the persistent configuration).
 hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* qa, const float* a_scale,
-                       const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out,
+                       const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out, int cus,
                        hipStream_t stream);
 
 // Per-token quantisation and the FP8 GEMM (configuration 0) in one launch. qa_ws [m, k]

@@ -169,9 +169,22 @@ def traffic_markdown(t, command):
     return "\n".join(out) + "\n"
 
 
+def _group_for(groups, name, grid):
+    """The (value, label) of the first group whose key matches a launch: a key is a grid
+    size, or (kernel-name substring, grid size) where two kernels share a grid size."""
+    for key, val in groups.items():
+        if isinstance(key, tuple):
+            if key[1] == grid and key[0] in name:
+                return key, val
+        elif key == grid:
+            return key, val
+    return None, None
+
+
 def counters(csv_path, kernel, groups=None):
     """Median per launch of every counter in a ``--pmc`` run, for the kernels matching
-    `kernel`, grouped by grid size; `groups` maps grid sizes to (algorithmic flop, label).
+    `kernel`, one record per (kernel, grid size); `groups` maps grid sizes, or
+    (kernel-name substring, grid size) pairs, to (algorithmic flop, label).
 
     rocprofv3 sums a counter over all its hardware instances, so GRBM_GUI_ACTIVE (one
     per XCD) reads the XCD count times the kernel's busy cycles, and
@@ -185,7 +198,7 @@ def counters(csv_path, kernel, groups=None):
     for r in csv.DictReader(open(csv_path)):
         if kernel not in r["Kernel_Name"]:
             continue
-        g = int(r["Grid_Size"])
+        g = (r["Kernel_Name"], int(r["Grid_Size"]))
         d = per.setdefault(g, {"names": set(), "counters": {}, "dur": {}})
         d["names"].add(r["Kernel_Name"])
         d["counters"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -195,16 +208,21 @@ def counters(csv_path, kernel, groups=None):
     if not per:
         raise ValueError(f"kernel {kernel!r} not found in {csv_path}")
     groups = dict(groups or {})
+    keys = list(groups)
+    matched = {g: _group_for(groups, g[0], g[1]) for g in per}
+    # launches named by a group first, in the groups' order, then the rest
+    order = sorted(per, key=lambda g: (keys.index(matched[g][0]) if matched[g][0] is not None else len(keys),
+                                       g[1], g[0]))
     out = []
-    for g in [x for x in groups if x in per] + sorted(x for x in per if x not in groups):
+    for g in order:
         d = per[g]
         med = {c: statistics.median(v) for c, v in d["counters"].items()}
-        rec = {"grid_size": g, "kernel": sorted(d["names"])[0],
+        rec = {"grid_size": g[1], "kernel": g[0],
                "launches": max(len(v) for v in d["counters"].values()), "counters": med}
         if d["dur"]:
             rec["duration_us"] = statistics.median(d["dur"].values()) * 1e6
-        if g in groups:
-            rec["algorithmic_flop"], rec["label"] = groups[g]
+        if matched[g][0] is not None:
+            rec["algorithmic_flop"], rec["label"] = matched[g][1]
         gui = med.get("GRBM_GUI_ACTIVE")
         if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
             rec["mfma_busy"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / XCDS * SIMDS)
@@ -294,7 +312,9 @@ def main(argv=None):
     d = sub.add_parser("counters")
     d.add_argument("csv")
     d.add_argument("--kernel", required=True)
-    d.add_argument("--group", action="append", default=[], metavar="GRID=FLOP[:LABEL]")
+    d.add_argument("--group", action="append", default=[], metavar="[NAME@]GRID=FLOP[:LABEL]",
+                   help="algorithmic flop (and a label) of the launches with this grid size, or of those "
+                        "whose kernel name contains NAME and have this grid size")
     d.add_argument("--command", required=True)
     d.add_argument("--out")
     d.add_argument("--json")
@@ -311,9 +331,10 @@ def main(argv=None):
     elif args.cmd == "counters":
         groups = {}
         for g in args.group:
-            grid, rest = g.split("=", 1)
+            key, rest = g.split("=", 1)
             flop, _, label = rest.partition(":")
-            groups[int(grid)] = (float(flop), label or f"grid {grid}")
+            name, at, grid = key.rpartition("@")
+            groups[(name, int(grid)) if at else int(grid)] = (float(flop), label or f"grid {grid}")
         recs = counters(args.csv, args.kernel, groups)
         text = counters_markdown(recs, args.command)
         if args.json:

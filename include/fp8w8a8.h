@@ -256,8 +256,10 @@ int fp8_linear(const void* a, int a_kind, const float* a_scale, int64_t m, int64
  * Introspection of the construction-time choice (for tests and reports).
  * fp8_linear_plan_config writes, for an activation with m rows, the id of the GEMM
  * kernel configuration the plan launches and its tile (block rows in m, block
- * columns in n), and the number of workgroups. Returns FP8W8A8_ERR_INVALID_ARG for
- * a NULL plan or output pointer.
+ * columns in n), and the number of output tiles: one workgroup each, except in the
+ * persistent configuration (6), which launches one workgroup per compute unit (the
+ * count rounded down to a multiple of 8, at most the tile count) that walks them.
+ * Returns FP8W8A8_ERR_INVALID_ARG for a NULL plan or output pointer.
  */
 int fp8_linear_plan_config(const fp8_linear_plan* plan, int64_t m, int* config_id, int* tile_m,
                            int* tile_n, int64_t* workgroups);

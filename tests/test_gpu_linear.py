@@ -5,7 +5,8 @@ the same bf16 inputs (the oracle quantises them itself): elementwise
 |gpu - ref| <= 1e-2 (|ref| + 1) and relative Frobenius error <= 2e-3. Quantised
 activations and weights are compared bit for bit on the way. Covered: the tiny
 config in full; every compiled GEMM configuration on ragged m / n / k tails; the
-selector's plans at the four full-size workloads, every output element against the
+persistent configuration where each of its workgroups walks several tiles (whole output,
+and bit for bit against one workgroup per tile); the selector's plans at the four full-size workloads, every output element against the
 oracle (elementwise bound on each, relative Frobenius error over the whole output) and
 every activation code and scale bit for bit; the e4m3fn pass-through input on the
 oracle's own codes; A = 0 (output == bias exactly); no bias; guard bands.
@@ -58,6 +59,9 @@ TAIL_SHAPES = [(1, 16, 16), (26, 144, 48), (63, 16, 272), (65, 144, 16), (257, 1
                (513, 528, 1040)]
 
 
+PERSISTENT = 6  # the 256 x 256 tiles walked by one workgroup per CU
+
+
 @pytest.mark.parametrize("config", range(N_CONFIGS))
 @pytest.mark.parametrize("m,n,k", TAIL_SHAPES)
 def test_every_config_on_ragged_tails(config, m, n, k):
@@ -71,6 +75,32 @@ def test_every_config_on_ragged_tails(config, m, n, k):
     out = gemm_run_config(config, t(qa), t(sa), t(qw), t(sw), case.bias.to(dev))
     torch.cuda.synchronize()
     assert_linear_close(out, ref, f"config {config} {m}x{n}x{k}")
+
+
+# more tiles than compute units, ragged in m, n and k (a one-stage k among them): every
+# workgroup of the persistent configuration walks several tiles, each handing its stage
+# ring to the next before its epilogue
+PERSISTENT_SHAPES = [(4100, 12304, 272), (8200, 8208, 208), (8197, 8208, 128), (16400, 4112, 144)]
+
+
+@pytest.mark.parametrize("m,n,k", PERSISTENT_SHAPES)
+def test_persistent_config_walks_many_tiles(m, n, k):
+    dev = require_gpu()
+    tiles = -(-m // 256) * -(-n // 256)
+    assert tiles > 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    case = make_case(m, n, k, seed=m + n + k, kind="outlier")
+    qa, sa = cref.quant_rows(bf16_bits(case.a))
+    qw, sw = _oracle_weight(case.w)
+    bias_bits = _bias_bits(case.bias)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    args = (t(qa), t(sa), t(qw), t(sw), case.bias.to(dev))
+    out = gemm_run_config(PERSISTENT, *args)
+    out0 = gemm_run_config(0, *args)
+    torch.cuda.synchronize()
+    # the same products summed in the same order as one workgroup per tile
+    assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+    assert_linear_close_rows(out, lambda r0, r1: ol.linear_ref_fp8(qa[r0:r1], sa[r0:r1], qw, sw, bias_bits),
+                             f"persistent {m}x{n}x{k}")
 
 
 def test_zero_activation_gives_bias_exactly():
@@ -260,9 +290,12 @@ def test_selector_picks_the_measured_best_at_the_page_shapes():
     up = Fp8Linear(torch.zeros((8192, 2048), dtype=torch.bfloat16, device=dev))
     down = Fp8Linear(torch.zeros((2048, 8192), dtype=torch.bfloat16, device=dev))
     qkv = Fp8Linear(torch.zeros((2048, 2048), dtype=torch.bfloat16, device=dev))
-    assert up.config(4096)[0] == 0
+    # the persistent form of the 256 x 256 tiles where every CU gets two or more tiles
+    # and k is 2048 .. 4096; one workgroup per tile at k = 8192
+    assert up.config(4096)[0] == PERSISTENT and up.config(32760)[0] == PERSISTENT
     assert down.config(4096)[0] == 2
-    assert qkv.config(32760)[0] == 0 and down.config(32760)[0] == 0
+    assert qkv.config(32760)[0] == PERSISTENT and down.config(32760)[0] == 0
+    assert up.config(1024)[0] != PERSISTENT  # 128 tiles: one round
     assert qkv.config(26)[0] == 5 and up.config(26)[0] == 5 and down.config(26)[0] == 5
     assert qkv.config(64)[0] == 4
 

@@ -128,3 +128,23 @@ def test_counters_mfma_busy_share(tmp_path):
     assert r["mfma_flop"] == pytest.approx(5.12e8)
     assert r["duration_us"] == pytest.approx(50.0) and r["gui_clock_ghz"] == pytest.approx(2.0)
     assert "| matrix-core busy share" in profiling.counters_markdown(recs, "cmd")
+
+
+def test_counters_two_kernels_on_one_grid_size(tmp_path):
+    # the persistent 256 x 256 GEMM (256 workgroups) and the 128 x 256 tiles at FFN-down
+    # (256 tiles) both launch 131072 work-items: records per kernel, labels by name
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for d, (name, busy) in enumerate([("gemm<256, 256, true>", 50_000), ("gemm<128, 256, false>", 70_000)] * 2):
+            row = {"Dispatch_Id": d, "Kernel_Name": name, "Grid_Size": 131072}
+            w.writerow(dict(row, Counter_Name="GRBM_GUI_ACTIVE", Counter_Value=8 * 100_000))
+            w.writerow(dict(row, Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES", Counter_Value=1024 * busy))
+    groups = {("<256, 256", 131072): (1.0, "FFN-up"), ("<128, 256", 131072): (2.0, "FFN-down")}
+    recs = profiling.counters(str(p), "gemm", groups)
+    assert [r["label"] for r in recs] == ["FFN-up", "FFN-down"]
+    assert [r["launches"] for r in recs] == [2, 2]
+    assert recs[0]["mfma_busy"] == pytest.approx(0.5) and recs[1]["mfma_busy"] == pytest.approx(0.7)
+    assert recs[1]["algorithmic_flop"] == 2.0
