@@ -46,6 +46,14 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) 
                : "memory");
 }
 
+// The same for 4 bytes per lane: lane i's dword lands at LDS address lds + 4 i.
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voffset) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 

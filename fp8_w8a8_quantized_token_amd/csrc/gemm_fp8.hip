@@ -242,7 +242,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "tile / wave mismatch");
   static_assert(kRowGroups % kWaves == 0, "fill work must split evenly across waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
-  constexpr int kEpiBytes = (BM + 2 * BN) * 4;  // the tile's a_scale, w_scale, bias (fp32)
+  // the tile's epilogue operands in LDS: a_scale [BM] and w_scale [BN] (fp32), bias [BN]
+  // (bf16), each region a whole number of 256-byte DMA chunks
+  constexpr int kEpiBiasBytes = (BN * 2 + 255) / 256 * 256;
+  constexpr int kEpiBytes = (BM + BN) * 4 + kEpiBiasBytes;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole DMA chunks of scales");
   // PERSIST's output staging: 32 token rows of the wave tile per wave; the epilogue
   // operands share the region (they are in registers while it holds output)
   constexpr int kPieceRows = 32;
@@ -297,24 +301,50 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
   v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
-  // Epilogue operands of this tile, one value per thread, requested now; they arrive
-  // with the first stage and are parked in LDS, so they hold no registers during the
+  // Epilogue operands of this tile, parked in LDS so they hold no registers during the
   // k loop.
   uint8_t* epi_base;
   if constexpr (PERSIST) epi_base = stage_buf<Tag, 8, kStagingBytes>();
   else epi_base = stage_buf<Tag, 7, kEpiBytes>();
   float* const epi_sa = reinterpret_cast<float*>(epi_base);
   float* const epi_sw = epi_sa + BM;
-  float* const epi_b = epi_sw + BN;
+  uint16_t* const epi_b16 = reinterpret_cast<uint16_t*>(epi_sw + BN);
   const int tid = threadIdx.x;
   const bool filler = wave < kFillWaves;
-  float pre_sa = 0.0f, pre_sw = 0.0f, pre_b = 0.0f;
-  if constexpr (!FUSED)
-    if (tid < BM && tid < rows_a) pre_sa = args.a_scale[m0 + tid];
-  if (tid < BN && tid < rows_w) {
-    pre_sw = args.w_scale[n0 + tid];
-    if (args.bias) pre_b = __uint_as_float((uint32_t)args.bias[n0 + tid] << 16);
-  }
+  // They come by 4-byte LDS DMA, issued by the filling waves before the tile's fills:
+  // 256-byte chunks (one wave-wide load each), a_scale first, then w_scale, then the bias;
+  // rows and channels past the tile's valid ones, and a missing bias, read zeros. Loaded
+  // into registers instead, they would be the only memory reads the compiler counts, and
+  // its wait for them (vmcnt(0): it cannot see the fills) would hold the first fills back
+  // by a whole memory round trip and then wait for every fill of the prologue.
+  constexpr int kEpiChunksA = BM / 64, kEpiChunksW = BN / 64;
+  constexpr int kEpiChunks = kEpiChunksA + kEpiChunksW + kEpiBiasBytes / 256;
+  auto issue_epi = [&](const float* a_scale, const float* w_scale, const uint16_t* bias, int em0, int en0,
+                       int erows_a, int erows_w) {
+    if (!filler) return;
+    const v4i rs_a = make_rsrc(a_scale + em0, (uint32_t)erows_a * 4u);
+    const v4i rs_w = make_rsrc(w_scale + en0, (uint32_t)erows_w * 4u);
+    const v4i rs_b = make_rsrc(bias ? bias + en0 : nullptr, bias ? (uint32_t)erows_w * 2u : 0u);
+    const uint32_t vo = 4u * (uint32_t)lane;
+#pragma unroll
+    for (int c0 = 0; c0 < kEpiChunks; c0 += kFillWaves) {
+      const int c = c0 + wave;  // uniform
+      if (c >= kEpiChunks) break;
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(epi_base + 256 * c);
+      if (c < kEpiChunksA) dma4(rs_a, dst, vo + 256u * (uint32_t)c);
+      else if (c < kEpiChunksA + kEpiChunksW) dma4(rs_w, dst, vo + 256u * (uint32_t)(c - kEpiChunksA));
+      else dma4(rs_b, dst, vo + 256u * (uint32_t)(c - kEpiChunksA - kEpiChunksW));
+    }
+  };
+  // (the single-launch form loads them into registers: its a_scale exists only after
+  // the quantisation phase, and it waits for everything before its k loop anyway)
+  float pre_sa = 0.0f, pre_sw = 0.0f;
+  uint32_t pre_b = 0;
+  if constexpr (FUSED)
+    if (tid < BN && tid < rows_w) {
+      pre_sw = args.w_scale[n0 + tid];
+      if (args.bias) pre_b = args.bias[n0 + tid];
+    }
 
   // Fill geometry: a wave-wide fill covers RPF rows x BK bytes = 1 KiB of a stage;
   // lane i writes bytes [16 i, 16 i + 16): row i / CPR of the group, position i % CPR,
@@ -360,17 +390,20 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       const bool odd = ((fwave * RPF) & 15) != 0;
       const bool kvalid = odd ? kvalid1 : kvalid0;
       const uint32_t v0 = (uint32_t)(fwave * RPF) * (uint32_t)fK + (odd ? foff1 : foff0) + (uint32_t)k0;
-      uint32_t stride = (uint32_t)(kFillWaves * RPF) * (uint32_t)fK;
-      asm volatile("" : "+s"(stride));
-      stride = (uint32_t)__builtin_amdgcn_readfirstlane((int)stride);
-      // (the compiler forms v0 + j * stride as one 64-bit multiply-add per fill; every
-      // formulation with plain adds measured here tipped the loop into spilling)
+      uint32_t kk = (uint32_t)fK;
+      asm volatile("" : "+s"(kk));
+      kk = (uint32_t)__builtin_amdgcn_readfirstlane((int)kk);
+      // Fill j's first row lies (j mod FA) * kFillWaves * RPF rows (< 2^8) past the base,
+      // and k < 2^24, so the row offset is an exact 24-bit product: a full-rate
+      // multiply-add per fill (a 32-bit product becomes a quarter-rate 64-bit one; every
+      // formulation with plain adds measured here tipped the loop into spilling).
+      static_assert((FA - 1) * kFillWaves * RPF < (1 << 8) && FP8W8A8_MAX_DIM < (1 << 24), "24-bit row offsets");
 #pragma unroll
       for (int j = 0; j < F; ++j) {
         if ((part == 1 && j >= FA) || (part == 2 && j < FA)) continue;
         const int g = fwave + j * kFillWaves;
         const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024);
-        const uint32_t vo = v0 + (uint32_t)(j < FA ? j : j - FA) * stride;
+        const uint32_t vo = v0 + __umul24(kk, (uint32_t)((j < FA ? j : j - FA) * kFillWaves * RPF));
         dma16(j < FA ? rsrc_a : rsrc_w, dst, kvalid ? vo : kOutOfRange);
       }
       return;
@@ -500,26 +533,30 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     if (filler && nst > 1) wait_vm_lgkm0<FA>();
     else wait_vm_lgkm0<0>();
   } else if constexpr (kPrologueAll) {
+    issue_epi(args.a_scale, args.w_scale, args.bias, m0, n0, rows_a, rows_w);
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue_all(buf(s), s * BK);
-    // PERSIST waits for both first stages here, as it does for every later tile
-    if constexpr (PERSIST) wait_vm_lgkm0<0>();
-    else wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
+    // stage 0 complete (and the epilogue operands, requested before it)
+    wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
   } else {
+    issue_epi(args.a_scale, args.w_scale, args.bias, m0, n0, rows_a, rows_w);
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue(buf(s), s * BK);
     if (filler) wait_stage<F, STAGES>(min(nst - 1, STAGES - 1));
     else wait_vm_lgkm0<0>();
   }
-  // the epilogue operands were requested before the fills: the wait covered them
-  if (tid < BM) epi_sa[tid] = pre_sa;
-  if (tid < BN) {
-    epi_sw[tid] = pre_sw;
-    epi_b[tid] = pre_b;
+  if constexpr (FUSED) {
+    // the wait above covered these loads
+    if (tid < BM) epi_sa[tid] = pre_sa;
+    if (tid < BN) {
+      epi_sw[tid] = pre_sw;
+      epi_b16[tid] = (uint16_t)pre_b;
+    }
   }
   block_barrier();
+  bool first_tile = true;  // PERSIST: the first tile's prologue left its second stage in flight
 
   auto sub = [&](int u, int s, int h, Frags& cur, Frags& nxt) {
     // s = stage index of u modulo STAGES, h = half of u (compile-time after unrolling)
@@ -527,10 +564,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     if (h == H - 1) {
       if (t + 1 < nst) {
         // stage t + 1 complete: the first stages came from every wave (FW each), later
-        // ones from the filling waves (F each). PERSIST: both first stages were waited
-        // for before the loop, and the previous tile's output stores may still be in
-        // flight; a wave that issues no refills has nothing else outstanding.
-        if (PERSIST && t == 0) wait_vm_lgkm0<63>();
+        // ones from the filling waves (F each). PERSIST, after the first tile: both first
+        // stages were waited for before the loop, and the previous tile's output stores
+        // may still be in flight; a wave that issues no refills has nothing else it waits for.
+        if (PERSIST && t == 0 && !first_tile) wait_vm_lgkm0<63>();
         else if (kPrologueAll && t == 0) wait_stage<FW, STAGES>(min(nst - 2, STAGES - 2));
         else if (filler) wait_stage<F, STAGES>(min(nst - 2 - t, STAGES - 2));
         else if (PERSIST) wait_vm_lgkm0<63>();
@@ -580,7 +617,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   // (PERSIST: the lane id goes through an empty asm so that the epilogue's per-lane
   // addresses are formed here, not hoisted above the k loop and held through it)
   int elane = lane;
-  if constexpr (PERSIST) asm volatile("" : "+v"(elane));
+  if constexpr (PERSIST) {
+    asm volatile("" : "+v"(elane));
+    // this tile's epilogue operands were requested by the filling waves after the
+    // previous tile's output; the second stage barrier of the loop (nst >= 3) came after
+    // their vmcnt(0), otherwise wait for them here
+    if (!first_tile && nst < 3) {
+      wait_vm_lgkm0<0>();
+      block_barrier();
+    }
+  }
   float r_sa[FM];
   float4 r_sw[FN][4], r_b[FN][4];
 #pragma unroll
@@ -591,7 +637,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     for (int q = 0; q < 4; ++q) {
       const int nl = wn * WTN + i * 32 + 8 * q + 4 * (elane >> 5);
       r_sw[i][q] = *reinterpret_cast<const float4*>(epi_sw + nl);
-      r_b[i][q] = *reinterpret_cast<const float4*>(epi_b + nl);
+      const uint2 b2 = *reinterpret_cast<const uint2*>(epi_b16 + nl);  // four bf16 -> fp32 exactly
+      r_b[i][q] = make_float4(__uint_as_float(b2.x << 16), __uint_as_float(b2.x & 0xffff0000u),
+                              __uint_as_float(b2.y << 16), __uint_as_float(b2.y & 0xffff0000u));
     }
   wait_vm_lgkm0<63>();
   block_barrier();
@@ -631,9 +679,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     const int nt = ra.tiles_m * ra.tiles_n;
     vtile += ra.shares;
     const bool more = vtile < nt;
-    pre_sa = 0.0f;  // (set on every path: no value carried round the tile loop)
-    pre_sw = 0.0f;
-    pre_b = 0.0f;
     if (more) {
       tile_coords_at<GROUP_M>(vtile, nt, ra.tiles_m, ra.tiles_n, tm, tn);
       tm = __builtin_amdgcn_readfirstlane(tm);
@@ -644,11 +689,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       rows_w = min(BN, ra.n - n0);
       rsrc_a = make_rsrc(ra.qa + (int64_t)m0 * ra.k, (uint32_t)rows_a * (uint32_t)ra.k);
       rsrc_w = make_rsrc(ra.qw + (int64_t)n0 * ra.k, (uint32_t)rows_w * (uint32_t)ra.k);
-      if (tid < BM && tid < rows_a) pre_sa = ra.a_scale[m0 + tid];
-      if (tid < BN && tid < rows_w) {
-        pre_sw = ra.w_scale[n0 + tid];
-        if (ra.bias) pre_b = __uint_as_float((uint32_t)ra.bias[n0 + tid] << 16);
-      }
       asm volatile("" : "+v"(foff0_), "+v"(foff1_), "+s"(fwave), "+s"(fK));
       fwave = __builtin_amdgcn_readfirstlane(fwave);
       fK = __builtin_amdgcn_readfirstlane(fK);
@@ -686,23 +726,22 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       store_wave_tile<kPieceRows, RC, true>(piece, elane, ra.out, ra.m, ra.n, er0 + j * 32, ec0);
     }
     if (!more) break;
-    // the next tile's fills and epilogue operands are older than this wave's kEpiStores
-    // stores; every wave has read its last piece before the operands overwrite the region
+    // the next tile's fills are older than this wave's kEpiStores stores; every wave
+    // has read its last piece before the next epilogue operands overwrite the region
     static_assert(kEpiStores < 64, "vmcnt range");
     wait_vm_lgkm0<kEpiStores>();
     block_barrier();
-    if (tid < BM) epi_sa[tid] = pre_sa;
-    if (tid < BN) {
-      epi_sw[tid] = pre_sw;
-      epi_b[tid] = pre_b;
+    {
+      const GemmArgs rb = reload_args();
+      issue_epi(rb.a_scale, rb.w_scale, rb.bias, m0, n0, rows_a, rows_w);
     }
+    first_tile = false;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    block_barrier();
   }
   }
 }
