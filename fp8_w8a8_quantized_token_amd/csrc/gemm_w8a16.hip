@@ -92,10 +92,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   static_assert(FA >= 1 && FW >= 1 && (BM / kARpf) % kFillWaves == 0 && (BN / kWRpf) % kFillWaves == 0,
                 "fills split evenly across the filling waves");
   static_assert(STAGES >= 2 && STAGES <= 6, "stage count");
-  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS budget of a CU");
+  // the tile's w_scale [BN] (fp32) and bias [BN] (bf16) in LDS, whole 256-byte DMA chunks
+  constexpr int kEpiBiasBytes = (BN * 2 + 255) / 256 * 256;
+  constexpr int kEpiBytes = BN * 4 + kEpiBiasBytes;
+  static_assert(BN % 64 == 0, "whole DMA chunks of scales");
+  static_assert(STAGES * kStageBytes + kEpiBytes <= 160 * 1024, "LDS budget of a CU");
   static_assert((STAGES - 1) * F < 64, "vmcnt range");
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
-  static_assert(2 * BN * 4 <= kStageBytes, "epilogue staging fits in one stage");
 
   auto buf = [](int s) -> uint8_t* {
     switch (s) {
@@ -122,12 +125,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   const v4i rsrc_a = make_rsrc(args.a + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K * 2u);
   const v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
-  const int tid = threadIdx.x;
-  float pre_sw = 0.0f, pre_b = 0.0f;
-  if (tid < BN && tid < rows_w) {
-    pre_sw = args.w_scale[n0 + tid];
-    if (args.bias) pre_b = __uint_as_float((uint32_t)args.bias[n0 + tid] << 16);
-  }
+  // The epilogue operands come by 4-byte LDS DMA from the filling waves, before their
+  // first fills (so the wait for stage 0 covers them): register loads would be the only
+  // reads the compiler counts, and its vmcnt(0) for them would hold the first fills back
+  // by a memory round trip. Channels past the tile and a missing bias read zeros.
+  uint8_t* const epi_base = stage_buf<Tag, 7, kEpiBytes>();
+  const float* const epi_sw = reinterpret_cast<const float*>(epi_base);
+  const uint16_t* const epi_b16 = reinterpret_cast<const uint16_t*>(epi_base + BN * 4);
 
   // Fill geometry. Activation: lane i writes row i / 8 of an 8-row group, chunk
   // position i % 8 holding logical chunk (i % 8) ^ swz<128>(row); the swizzle period
@@ -143,6 +147,21 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   const uint32_t fwoff = (uint32_t)fwr * (uint32_t)K + 16u * (uint32_t)fwc;
 
   const bool filler = wave < kFillWaves;
+  constexpr int kEpiChunksW = BN / 64, kEpiChunks = kEpiChunksW + kEpiBiasBytes / 256;
+  auto issue_epi = [&]() {
+    if (!filler) return;
+    const v4i rs_w = make_rsrc(args.w_scale + n0, (uint32_t)rows_w * 4u);
+    const v4i rs_b = make_rsrc(args.bias ? args.bias + n0 : nullptr, args.bias ? (uint32_t)rows_w * 2u : 0u);
+    const uint32_t vo = 4u * (uint32_t)lane;
+#pragma unroll
+    for (int c0 = 0; c0 < kEpiChunks; c0 += kFillWaves) {
+      const int c = c0 + wave;  // uniform
+      if (c >= kEpiChunks) break;
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(epi_base + 256 * c);
+      if (c < kEpiChunksW) dma4(rs_w, dst, vo + 256u * (uint32_t)c);
+      else dma4(rs_b, dst, vo + 256u * (uint32_t)(c - kEpiChunksW));
+    }
+  };
   auto issue = [&](uint8_t* base, int s) {
     if (!filler) return;
     const int ke0 = s * KE;  // first k element of the stage
@@ -243,6 +262,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   // frees stage t's buffer, which is refilled with stage t + STAGES.
   const int nst = (K + KE - 1) / KE;
   const int nsub = nst * H;
+  issue_epi();
   if constexpr (kPrologueAll) {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
@@ -286,8 +306,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     }
   }
 
-  // Epilogue: the FP8 GEMM's (scale and bias through LDS into registers, one rounding
-  // to bf16, the tile staged per wave in LDS and stored as whole rows), without an
+  // Epilogue: the FP8 GEMM's (scale and bias from LDS into registers, one rounding to
+  // bf16, the tile staged per wave in LDS and stored as whole rows), without an
   // activation scale.
   constexpr int RC = WTN / 8;
   constexpr int kWaveOutBytes = WTM * WTN * 2;
@@ -295,15 +315,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   static_assert(kWavesPerBuf >= 1 && (kWaves + kWavesPerBuf - 1) / kWavesPerBuf <= STAGES,
                 "output staging fits in the stage buffers");
   static_assert(64 % RC == 0 && (WTM * RC) % 64 == 0, "row segments tile the wavefront");
-  float* epi_sw = reinterpret_cast<float*>(buf(0));
-  float* epi_b = epi_sw + BN;
-  block_barrier();
-  if (tid < BN) {
-    epi_sw[tid] = pre_sw;
-    epi_b[tid] = pre_b;
-  }
-  wait_vm_lgkm0<63>();
-  block_barrier();
   float4 r_sw[FN][4], r_b[FN][4];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -311,7 +322,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     for (int q = 0; q < 4; ++q) {
       const int nl = wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
       r_sw[i][q] = *reinterpret_cast<const float4*>(epi_sw + nl);
-      r_b[i][q] = *reinterpret_cast<const float4*>(epi_b + nl);
+      const uint2 b2 = *reinterpret_cast<const uint2*>(epi_b16 + nl);  // four bf16 -> fp32 exactly
+      r_b[i][q] = make_float4(__uint_as_float(b2.x << 16), __uint_as_float(b2.x & 0xffff0000u),
+                              __uint_as_float(b2.y << 16), __uint_as_float(b2.y & 0xffff0000u));
     }
   wait_vm_lgkm0<63>();
   block_barrier();
