@@ -68,6 +68,7 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP8_FLOP_PER_CU_CLK = 8192  # dense FP8 MFMA per CU per shader clock (5.0 PFLOP/s = 256 CUs x 8192 x 2.4 GHz)
 N_CUS = 256
+PERSISTENT_CONFIG = 6  # the persistent 256 x 256 GEMM form, the plan's choice at FFN-up
 TRAFFIC_FILES = {name: os.path.join(ROOT, "profiles", f"gemm_fp8_{name}_traffic.json") for name in ("ffn_up", "ffn_down")}
 # the FP8 GEMM kernel's sources (the committed counter record names the SHA-256 over both)
 GEMM_SOURCES = [os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", f) for f in ("gemm_fp8.hip", "gemm_common.h")]
@@ -279,9 +280,11 @@ def w8a16_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
 
 
 def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
-    """The FFN-up step as one launch (fp8_quant_gemm) against the same step as two
-    launches (fp8_quant_rows, then GEMM configuration 0), same inputs and loop shape:
-    events only at the ends of `steps` back-to-back steps."""
+    """The FFN-up step as one launch (fp8_quant_gemm, the 256 x 256 tiles of configuration
+    0) against the same step as two launches: fp8_quant_rows, then configuration 0 (the
+    same tiles), and fp8_quant_rows, then the configuration the plan runs at this shape
+    (the persistent 256 x 256 form, 6). Same inputs and loop shape, events only at the
+    ends of `steps` back-to-back steps."""
     from workloads.synth import activation, bias as gen_bias, weight
     from fp8_w8a8_quantized_token_amd import _lib
     sptr = ctypes.c_void_p(stream.cuda_stream)
@@ -304,17 +307,21 @@ def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
         if st:
             raise _lib.Fp8W8A8Error(st, "fp8_quant_gemm")
 
-    def two(i):
-        a, qw, sw, b, out, ws = sets[i % nsets]
-        scales = ctypes.c_void_p(ws.data_ptr() + codes_bytes)
-        st = lib.fp8_quant_rows(P(a), M, K, P(ws), scales, sptr)
-        st = st or lib.fp8_gemm_run_config(0, M, N, K, P(ws), scales, P(qw), P(sw), P(b), P(out), sptr)
-        if st:
-            raise _lib.Fp8W8A8Error(st, "fp8_quant_rows / fp8_gemm_run_config")
+    def two_with(config):
+        def two(i):
+            a, qw, sw, b, out, ws = sets[i % nsets]
+            scales = ctypes.c_void_p(ws.data_ptr() + codes_bytes)
+            st = lib.fp8_quant_rows(P(a), M, K, P(ws), scales, sptr)
+            st = st or lib.fp8_gemm_run_config(config, M, N, K, P(ws), scales, P(qw), P(sw), P(b), P(out), sptr)
+            if st:
+                raise _lib.Fp8W8A8Error(st, "fp8_quant_rows / fp8_gemm_run_config")
+        return two
 
+    two, two_p = two_with(0), two_with(PERSISTENT_CONFIG)
     res = {}
-    for name, run in (("two_launch", two), ("single_launch", one), ("two_launch_again", two),
-                      ("single_launch_again", one)):
+    for name, run in (("two_launch", two), ("single_launch", one), ("two_launch_persistent", two_p),
+                      ("two_launch_again", two), ("single_launch_again", one),
+                      ("two_launch_persistent_again", two_p)):
         preheat(torch, run)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -328,12 +335,16 @@ def quant_gemm_bench(torch, fp8, lib, dev, stream, steps, nsets=12):
     torch.cuda.empty_cache()
     two_us = min(res["two_launch"], res["two_launch_again"])
     one_us = min(res["single_launch"], res["single_launch_again"])
+    two_p_us = min(res["two_launch_persistent"], res["two_launch_persistent_again"])
     flop = 2.0 * M * N * K
     return {"kernel": "gemm_fp8_kernel (single-launch form)", "M": M, "N": N, "K": K, "steps": steps,
             "single_launch_us_per_step": round(one_us, 3), "two_launch_us_per_step": round(two_us, 3),
+            "two_launch_persistent_us_per_step": round(two_p_us, 3),
             "single_launch_tflops": round(flop / (one_us * 1e-6) / 1e12, 2),
             "two_launch_tflops": round(flop / (two_us * 1e-6) / 1e12, 2),
-            "speedup": round(two_us / one_us, 4)}
+            "two_launch_persistent_tflops": round(flop / (two_p_us * 1e-6) / 1e12, 2),
+            "speedup": round(two_us / one_us, 4),
+            "speedup_vs_persistent_two_launch": round(two_p_us / one_us, 4)}
 
 
 def block_bench(torch, fp8, lib, dev, stream, steps, config):
