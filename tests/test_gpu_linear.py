@@ -83,17 +83,18 @@ def test_every_config_on_ragged_tails(config, m, n, k):
 PERSISTENT_SHAPES = [(4100, 12304, 272), (8200, 8208, 208), (8197, 8208, 128), (16400, 4112, 144)]
 
 
-@pytest.mark.parametrize("m,n,k", PERSISTENT_SHAPES)
-def test_persistent_config_walks_many_tiles(m, n, k):
+@pytest.mark.parametrize("m,n,k,with_bias", [s + (True,) for s in PERSISTENT_SHAPES] + [(8200, 8208, 208, False)])
+def test_persistent_config_walks_many_tiles(m, n, k, with_bias):
     dev = require_gpu()
     tiles = -(-m // 256) * -(-n // 256)
     assert tiles > 2 * torch.cuda.get_device_properties(dev).multi_processor_count
     case = make_case(m, n, k, seed=m + n + k, kind="outlier")
     qa, sa = cref.quant_rows(bf16_bits(case.a))
     qw, sw = _oracle_weight(case.w)
-    bias_bits = _bias_bits(case.bias)
+    bias = case.bias if with_bias else None
+    bias_bits = _bias_bits(bias)
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-    args = (t(qa), t(sa), t(qw), t(sw), case.bias.to(dev))
+    args = (t(qa), t(sa), t(qw), t(sw), bias.to(dev) if bias is not None else None)
     out = gemm_run_config(PERSISTENT, *args)
     out0 = gemm_run_config(0, *args)
     torch.cuda.synchronize()
