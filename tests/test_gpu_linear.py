@@ -104,6 +104,39 @@ def test_persistent_config_walks_many_tiles(m, n, k, with_bias):
                              f"persistent {m}x{n}x{k}")
 
 
+def test_one_plan_on_two_streams_at_once():
+    # a plan is immutable after construction: runs on different streams (each with its
+    # own workspace) may overlap, here one on the persistent configuration (4096 tokens)
+    # and one on another (700 tokens), plus a second plan on a third stream
+    dev = require_gpu()
+    case = make_case(4096, 8192, 2048, seed=77, kind="outlier")
+    lin = Fp8Linear(case.w.to(dev), case.bias.to(dev))
+    other = Fp8Linear(make_case(16, 2048, 2048, seed=78).w.to(dev))
+    a1 = case.a.to(dev)
+    a2 = make_case(700, 8192, 2048, seed=79, kind="outlier").a.to(dev)
+    a3 = make_case(2000, 2048, 2048, seed=80).a.to(dev)
+    jobs = [(lin, a1), (lin, a2), (other, a3)]
+    assert lin.config(4096)[0] == PERSISTENT or torch.cuda.get_device_properties(dev).multi_processor_count != 256
+    serial = []
+    for p, a in jobs:
+        serial.append(p(a))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev) for _ in jobs]
+    outs = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        res = []
+        for st, (p, a) in zip(streams, jobs):
+            with torch.cuda.stream(st):
+                ws = torch.empty((p.workspace_bytes(a.shape[0]),), dtype=torch.uint8, device=dev)
+                res.append(p(a, workspace=ws))
+        torch.cuda.synchronize()
+        outs.append(res)
+    for res in outs:
+        for got, want in zip(res, serial):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
 def test_zero_activation_gives_bias_exactly():
     dev = require_gpu()
     case = make_case(70, 272, 256, seed=3)
