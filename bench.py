@@ -39,7 +39,8 @@ Other legs (outside the headline step; `--legs` selects them):
   quant_gemm    the FFN-up step as one launch against the two-launch step
   blocks        the QKV config (one quantisation of [32760, 2048], three GEMMs, the
                 26-row encoder input through the same weights) and the DiT block (4
-                quantisations, 6 GEMMs at 32760 tokens) as whole steps
+                quantisations, 6 GEMMs at 32760 tokens) as whole steps, the GEMMs on
+                one activation run as a group, beside the same step with separate calls
   cpu           the CPU oracle baseline
 
 `clocks` reads the shader and memory clocks with amd-smi while the FFN-up step runs
@@ -368,30 +369,52 @@ def block_bench(torch, fp8, lib, dev, stream, steps, config):
     order = [(name, [(layer, act_m) for layer, act, act_m, _, _ in layer_specs(config) if act == name])
              for name in acts]
 
-    def step(_i):
-        for name, layers in order:
-            a = acts[name]
-            q, sc = codes[name]
-            st = lib.fp8_quant_rows(p(a), a.shape[0], a.shape[1], p(q), p(sc), sptr)
-            if st:
-                raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
-            for layer, m in layers:
-                st = lib.fp8_linear_run(lins[layer]._plan, m, p(q), _lib.A_E4M3, p(sc), p(outs[layer]), None, 0,
-                                        sptr)
-                if st:
-                    raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
+    # the layers reading one activation go out as one group (fp8_linear_run_group: one
+    # persistent launch over all their tiles when each would take that form), and, for
+    # comparison, as separate fp8_linear_run calls
+    groups = {}
+    for name, layers in order:
+        g = len(layers)
+        groups[name] = ((ctypes.c_void_p * g)(*[lins[layer]._plan.value for layer, _ in layers]),
+                        (ctypes.c_void_p * g)(*[outs[layer].data_ptr() for layer, _ in layers]))
 
-    preheat(torch, step, batch=5)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def run(grouped):
+        def step(_i):
+            for name, layers in order:
+                a = acts[name]
+                q, sc = codes[name]
+                st = lib.fp8_quant_rows(p(a), a.shape[0], a.shape[1], p(q), p(sc), sptr)
+                if st:
+                    raise _lib.Fp8W8A8Error(st, "fp8_quant_rows")
+                if grouped:
+                    plans, optrs = groups[name]
+                    st = lib.fp8_linear_run_group(ctypes.cast(plans, ctypes.c_void_p), len(layers), layers[0][1], p(q),
+                                                  _lib.A_E4M3, p(sc), ctypes.cast(optrs, ctypes.c_void_p), None, 0,
+                                                  sptr)
+                    if st:
+                        raise _lib.Fp8W8A8Error(st, "fp8_linear_run_group")
+                    continue
+                for layer, m in layers:
+                    st = lib.fp8_linear_run(lins[layer]._plan, m, p(q), _lib.A_E4M3, p(sc), p(outs[layer]), None, 0,
+                                            sptr)
+                    if st:
+                        raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
+
+        preheat(torch, step, batch=5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_sep = run(False)
+    ms = run(True)
     res = {"quantisations": len(order), "gemms": len(lins), "steps": steps, "flop_per_step": flop,
            "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+           "grouped": True, "ms_per_step_separate_gemms": round(ms_sep, 4),
            "gemm_configs": {layer: lin.config(outs[layer].shape[0])[0] for layer, lin in lins.items()}}
     del acts, codes, lins, outs
     torch.cuda.empty_cache()

@@ -35,6 +35,7 @@ FMT_E5M2 = 1
 NOALLOC_SCRATCH_BYTES = 80 << 20
 
 MAX_ROWS = 1 << 24
+MAX_GROUP = 4
 MAX_DIM = 1 << 20
 
 _c_i64 = ctypes.c_int64
@@ -55,6 +56,8 @@ SIGNATURES = {
     "fp8_linear_workspace_bytes": (ctypes.c_size_t, [_c_p, _c_i64]),
     "fp8_linear_run": (ctypes.c_int, [_c_p, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "fp8_linear_run_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p]),
+    "fp8_linear_run_group": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, _c_p, ctypes.c_int, _c_p, _c_p, _c_p,
+                                            ctypes.c_size_t, _c_p]),
     "fp8_linear_destroy": (None, [_c_p]),
     "fp8_linear": (ctypes.c_int, [_c_p, ctypes.c_int, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                   ctypes.c_size_t, _c_p]),

@@ -467,6 +467,70 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 
+int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_t m, const void* a, int a_kind,
+                         const float* a_scale, void* const* outs_bf16, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!plans || !outs_bf16 || !a) return FP8W8A8_ERR_INVALID_ARG;
+  if (nplans < 1 || nplans > FP8W8A8_MAX_GROUP) return FP8W8A8_ERR_INVALID_ARG;
+  for (int i = 0; i < nplans; ++i)
+    if (!plans[i] || !outs_bf16[i]) return FP8W8A8_ERR_INVALID_ARG;
+  const fp8_linear_plan* p0 = plans[0];
+  for (int i = 1; i < nplans; ++i) {
+    if (plans[i]->k != p0->k) return FP8W8A8_ERR_BAD_SHAPE;
+    if (plans[i]->device != p0->device) return FP8W8A8_ERR_BAD_DEVICE;
+  }
+  if (a_kind != FP8W8A8_A_BF16 && a_kind != FP8W8A8_A_E4M3) return FP8W8A8_ERR_INVALID_ARG;
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  if (!aligned(a, 16)) return FP8W8A8_ERR_MISALIGNED;
+  for (int i = 0; i < nplans; ++i)
+    if (!aligned(outs_bf16[i], 16)) return FP8W8A8_ERR_MISALIGNED;
+  if (a_kind == FP8W8A8_A_E4M3) {
+    if (!a_scale) return FP8W8A8_ERR_INVALID_ARG;
+    if (!aligned(a_scale, 4)) return FP8W8A8_ERR_MISALIGNED;
+  } else {
+    if (!workspace) return FP8W8A8_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return FP8W8A8_ERR_MISALIGNED;
+    if (workspace_bytes < fp8_linear_workspace_bytes(p0, m)) return FP8W8A8_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (m == 0) return FP8W8A8_OK;
+  int st = plan_device_current(p0->device);
+  if (st != FP8W8A8_OK) return st;
+  // every plan's choice at this m; one launch when all of them take the persistent form
+  int config[FP8W8A8_MAX_GROUP];
+  bool grouped = nplans > 1;
+  for (int i = 0; i < nplans; ++i) {
+    config[i] = plan_bucket_config(plans[i], m);
+    if (!grid_fits(config[i], m, plans[i]->n)) return FP8W8A8_ERR_BAD_SHAPE;
+    if (config[i] != kW8A8Persistent) grouped = false;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* qa = static_cast<const uint8_t*>(a);
+  const float* sa = a_scale;
+  if (a_kind == FP8W8A8_A_BF16) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* ws_scale = reinterpret_cast<float*>(ws + align256((size_t)m * (size_t)p0->k));
+    if (launch_quant_rows(static_cast<const uint16_t*>(a), m, p0->k, ws, ws_scale, s) != hipSuccess)
+      return FP8W8A8_ERR_HIP;
+    qa = ws;
+    sa = ws_scale;
+  }
+  if (grouped) {
+    GroupProblem probs[FP8W8A8_MAX_GROUP];
+    for (int i = 0; i < nplans; ++i)
+      probs[i] = GroupProblem{plans[i]->w, plans[i]->w_scale, plans[i]->bias, static_cast<uint16_t*>(outs_bf16[i]),
+                              plans[i]->n};
+    return launch_gemm_group(m, p0->k, qa, sa, nplans, probs, p0->cu_count, s) == hipSuccess ? FP8W8A8_OK
+                                                                                            : FP8W8A8_ERR_HIP;
+  }
+  for (int i = 0; i < nplans; ++i) {
+    const fp8_linear_plan* p = plans[i];
+    if (launch_gemm(config[i], m, p->n, p->k, qa, sa, p->w, p->w_scale, p->bias, static_cast<uint16_t*>(outs_bf16[i]),
+                    p->cu_count, s) != hipSuccess)
+      return FP8W8A8_ERR_HIP;
+  }
+  return FP8W8A8_OK;
+}
+
 int fp8_linear_run_noalloc(const fp8_linear_plan* plan, int64_t m, const void* a, int a_kind, const float* a_scale,
                            void* out_bf16, void* stream) {
   if (!plan || !a || !out_bf16) return FP8W8A8_ERR_INVALID_ARG;

@@ -61,6 +61,9 @@
 namespace fp8w8a8 {
 namespace {
 
+// The persistent form runs up to kMaxGroup problems in one launch (see gemm_fp8_kernel).
+constexpr int kMaxGroup = FP8W8A8_MAX_GROUP;
+
 struct GemmArgs {
   const uint8_t* qa;
   const float* a_scale;
@@ -77,6 +80,16 @@ struct GemmArgs {
   unsigned long long* flags;
   unsigned long long epoch;
   int shares, rows_per_share;
+  // persistent form: problems 0 .. ngroup - 1 share qa, a_scale, m and k; problem p has its
+  // own weight, w_scale, bias, output and n, and owns the global tile columns
+  // [g_tn_end[p - 1], g_tn_end[p]) (from 0 for p = 0). One problem when ungrouped.
+  int ngroup;
+  int g_tn_end[kMaxGroup];
+  int g_n[kMaxGroup];
+  const uint8_t* g_qw[kMaxGroup];
+  const float* g_ws[kMaxGroup];
+  const uint16_t* g_bias[kMaxGroup];
+  uint16_t* g_out[kMaxGroup];
 };
 
 // The kernel's arguments read afresh from the kernel-argument segment. The address goes
@@ -84,13 +97,16 @@ struct GemmArgs {
 // a persistent workgroup that needs them again only after its k loop does not hold them
 // in scalar registers through it.
 typedef const __attribute__((address_space(4))) GemmArgs* KernargGemmArgs;
-__device__ __forceinline__ GemmArgs reload_args() {
+__device__ __forceinline__ KernargGemmArgs kernarg_args() {
   uint64_t p = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
   asm volatile("" : "+s"(p));
   // (the compiler takes an asm result as divergent; the address is uniform)
   p = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
-  const KernargGemmArgs k = reinterpret_cast<KernargGemmArgs>(p);
+  return reinterpret_cast<KernargGemmArgs>(p);
+}
+__device__ __forceinline__ GemmArgs reload_args() {
+  const KernargGemmArgs k = kernarg_args();
   GemmArgs r{};
   r.qa = k->qa;
   r.a_scale = k->a_scale;
@@ -104,6 +120,34 @@ __device__ __forceinline__ GemmArgs reload_args() {
   r.tiles_m = k->tiles_m;
   r.tiles_n = k->tiles_n;
   r.shares = k->shares;
+  return r;
+}
+
+// The problem a global tile column belongs to (persistent form), and the tile's first
+// column within that problem's output.
+struct TileProblem {
+  const uint8_t* qw;
+  const float* ws;
+  const uint16_t* bias;
+  uint16_t* out;
+  int n, n0;
+};
+template <int BN>
+__device__ __forceinline__ TileProblem tile_problem(KernargGemmArgs k, int tn) {
+  int p = 0, first = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < kMaxGroup; ++i)
+    if (i + 1 < k->ngroup && tn >= k->g_tn_end[i]) {
+      p = i + 1;
+      first = k->g_tn_end[i];
+    }
+  TileProblem r;
+  r.qw = k->g_qw[p];
+  r.ws = k->g_ws[p];
+  r.bias = k->g_bias[p];
+  r.out = k->g_out[p];
+  r.n = k->g_n[p];
+  r.n0 = (tn - first) * BN;
   return r;
 }
 
@@ -294,12 +338,26 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   tn = __builtin_amdgcn_readfirstlane(tn);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  int m0 = tm * BM, n0 = tn * BN;
+  // the weight side of this tile: the launch's own, or (PERSIST) its problem's
+  const uint8_t* w_base = args.qw;
+  const float* ws_base = args.w_scale;
+  const uint16_t* b_base = args.bias;
+  int n_cur = args.n;
+  int n0 = tn * BN;
+  if constexpr (PERSIST) {
+    const TileProblem pr = tile_problem<BN>(kernarg_args(), tn);
+    w_base = pr.qw;
+    ws_base = pr.ws;
+    b_base = pr.bias;
+    n_cur = pr.n;
+    n0 = pr.n0;
+  }
+  int m0 = tm * BM;
   const int K = args.k;
   int rows_a = min(BM, args.m - m0);
-  int rows_w = min(BN, args.n - n0);
+  int rows_w = min(BN, n_cur - n0);
   v4i rsrc_a = make_rsrc(args.qa + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
-  v4i rsrc_w = make_rsrc(args.qw + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
+  v4i rsrc_w = make_rsrc(w_base + (int64_t)n0 * K, (uint32_t)rows_w * (uint32_t)K);
 
   // Epilogue operands of this tile, parked in LDS so they hold no registers during the
   // k loop.
@@ -533,14 +591,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     if (filler && nst > 1) wait_vm_lgkm0<FA>();
     else wait_vm_lgkm0<0>();
   } else if constexpr (kPrologueAll) {
-    issue_epi(args.a_scale, args.w_scale, args.bias, m0, n0, rows_a, rows_w);
+    issue_epi(args.a_scale, ws_base, b_base, m0, n0, rows_a, rows_w);
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue_all(buf(s), s * BK);
     // stage 0 complete (and the epilogue operands, requested before it)
     wait_stage<FW, STAGES>(min(nst - 1, STAGES - 1));
   } else {
-    issue_epi(args.a_scale, args.w_scale, args.bias, m0, n0, rows_a, rows_w);
+    issue_epi(args.a_scale, ws_base, b_base, m0, n0, rows_a, rows_w);
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
       if (s < nst) issue(buf(s), s * BK);
@@ -675,7 +733,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     // Every wave has read the ring and this tile's epilogue operands (barrier above).
     // (args.shares holds the persistent grid size)
     const GemmArgs ra = reload_args();
-    const int er0 = m0 + wm * WTM, ec0 = n0 + wn * WTN;
+    const TileProblem cur = tile_problem<BN>(kernarg_args(), tn);  // this tile's output
+    const int er0 = m0 + wm * WTM, ec0 = cur.n0 + wn * WTN;
     const int nt = ra.tiles_m * ra.tiles_n;
     vtile += ra.shares;
     const bool more = vtile < nt;
@@ -683,12 +742,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       tile_coords_at<GROUP_M>(vtile, nt, ra.tiles_m, ra.tiles_n, tm, tn);
       tm = __builtin_amdgcn_readfirstlane(tm);
       tn = __builtin_amdgcn_readfirstlane(tn);
+      const TileProblem nx = tile_problem<BN>(kernarg_args(), tn);
       m0 = tm * BM;
-      n0 = tn * BN;
+      n0 = nx.n0;
       rows_a = min(BM, ra.m - m0);
-      rows_w = min(BN, ra.n - n0);
+      rows_w = min(BN, nx.n - n0);
       rsrc_a = make_rsrc(ra.qa + (int64_t)m0 * ra.k, (uint32_t)rows_a * (uint32_t)ra.k);
-      rsrc_w = make_rsrc(ra.qw + (int64_t)n0 * ra.k, (uint32_t)rows_w * (uint32_t)ra.k);
+      rsrc_w = make_rsrc(nx.qw + (int64_t)n0 * ra.k, (uint32_t)rows_w * (uint32_t)ra.k);
       asm volatile("" : "+v"(foff0_), "+v"(foff1_), "+s"(fwave), "+s"(fK));
       fwave = __builtin_amdgcn_readfirstlane(fwave);
       fK = __builtin_amdgcn_readfirstlane(fK);
@@ -723,7 +783,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
           *reinterpret_cast<uint2*>(piece + r * (RC * 16) + ((chunk ^ (r % RC)) << 4) + (half << 3)) =
               make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         }
-      store_wave_tile<kPieceRows, RC, true>(piece, elane, ra.out, ra.m, ra.n, er0 + j * 32, ec0);
+      store_wave_tile<kPieceRows, RC, true>(piece, elane, cur.out, ra.m, cur.n, er0 + j * 32, ec0);
     }
     if (!more) break;
     // the next tile's fills are older than this wave's kEpiStores stores; every wave
@@ -732,8 +792,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     wait_vm_lgkm0<kEpiStores>();
     block_barrier();
     {
-      const GemmArgs rb = reload_args();
-      issue_epi(rb.a_scale, rb.w_scale, rb.bias, m0, n0, rows_a, rows_w);
+      const KernargGemmArgs kb = kernarg_args();
+      const TileProblem nx = tile_problem<BN>(kb, tn);
+      issue_epi(kb->a_scale, nx.ws, nx.bias, m0, n0, rows_a, rows_w);
     }
     first_tile = false;
 #pragma unroll
@@ -754,6 +815,19 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
+  if (PERSIST) {
+    if (a.ngroup > 0) {
+      args.tiles_n = a.g_tn_end[a.ngroup - 1];  // the problems' tiles side by side
+    } else {  // one problem: the launch's own
+      args.ngroup = 1;
+      args.g_tn_end[0] = args.tiles_n;
+      args.g_n[0] = a.n;
+      args.g_qw[0] = a.qw;
+      args.g_ws[0] = a.w_scale;
+      args.g_bias[0] = a.bias;
+      args.g_out[0] = a.out;
+    }
+  }
   const int64_t tiles = (int64_t)args.tiles_m * args.tiles_n;
   int64_t wgs = tiles;
   if (PERSIST) {
@@ -950,6 +1024,25 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 6: return launch<256, 256, 2, 4, 2, 128, 4, false, true>(a, stream, cus);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_group(int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
+                             const GroupProblem* probs, int cus, hipStream_t stream) {
+  if (nprob < 1 || nprob > kMaxGroup) return hipErrorInvalidValue;
+  GemmArgs a{qa, a_scale, probs[0].qw, probs[0].w_scale, probs[0].bias, probs[0].out, (int)m, (int)probs[0].n,
+             (int)k, 0, 0};
+  a.ngroup = nprob;
+  int tn = 0;
+  for (int p = 0; p < nprob; ++p) {
+    tn += (int)((probs[p].n + 255) / 256);  // the persistent form's 256-column tiles
+    a.g_tn_end[p] = tn;
+    a.g_n[p] = (int)probs[p].n;
+    a.g_qw[p] = probs[p].qw;
+    a.g_ws[p] = probs[p].w_scale;
+    a.g_bias[p] = probs[p].bias;
+    a.g_out[p] = probs[p].out;
+  }
+  return launch<256, 256, 2, 4, 2, 128, 4, false, true>(a, stream, cus);
 }
 
 hipError_t launch_quant_gemm(int64_t m, int64_t n, int64_t k, const uint16_t* a_bf16, uint8_t* qa_ws, float* sa_ws,

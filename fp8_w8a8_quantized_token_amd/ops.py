@@ -239,12 +239,72 @@ class Fp8Linear:
             _require(out, (torch.bfloat16,), "out")
             if out.numel() != m * self.n:
                 raise ValueError("out has the wrong size")
+        if m == 0:  # nothing to compute (an empty tensor has no device address to pass)
+            return out.reshape(*lead, self.n)
         check(lib().fp8_linear_run(self._plan, m, _ptr(x2), kind, _ptr(x_scale) if fp8_in else None, _ptr(out),
                                    _ptr(ws), ws_bytes if ws is None else ws.numel(), _stream(x2)),
               "fp8_linear_run")
         return out.reshape(*lead, self.n)
 
     __call__ = forward
+
+
+def linear_group(linears, x, x_scale=None, outs=None, workspace=None):
+    """Several Fp8Linear layers on one input: [out_i [..., n_i]], bit-identical to
+    [lin(x) for lin in linears], with x quantised once.
+
+    The retrospective (aigcage.com, section 3.4) feeds one set of hidden states into the
+    Q, K and V projections; per-token quantisation of that input serves all of them, and
+    when every layer takes the library's persistent GEMM form at this many tokens the
+    products run as one launch (include/fp8w8a8.h, fp8_linear_run_group).
+    """
+    linears = list(linears)
+    if not 1 <= len(linears) <= _lib.MAX_GROUP:
+        raise ValueError(f"linear_group takes 1..{_lib.MAX_GROUP} layers, got {len(linears)}")
+    k = linears[0].k
+    if any(lin.k != k for lin in linears):
+        raise ValueError("every layer of a group must take the same number of input features")
+    if x.shape[-1] != k:
+        raise ValueError(f"input has {x.shape[-1]} features, the weights expect {k}")
+    lead = x.shape[:-1]
+    fp8_in = x.dtype in (torch.float8_e4m3fn, torch.uint8)
+    x2 = _codes(x).reshape(-1, k).contiguous()
+    m = x2.shape[0]
+    if fp8_in:
+        if x_scale is None:
+            raise ValueError("an e4m3fn input needs its per-token scale")
+        _require(x2, (torch.uint8,), "x", 2)
+        _require(x_scale, (torch.float32,), "x_scale", 1)
+        if x_scale.shape[0] != m:
+            raise ValueError("x_scale must have one entry per token")
+        kind, ws, ws_bytes = A_E4M3, None, 0
+    else:
+        _require(x2, (torch.bfloat16,), "x", 2)
+        kind = A_BF16
+        ws_bytes = linears[0].workspace_bytes(m)
+        if workspace is None:
+            workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=x2.device)
+        ws = workspace
+    if outs is None:
+        outs = [torch.empty((m, lin.n), dtype=torch.bfloat16, device=x2.device) for lin in linears]
+    else:
+        outs = list(outs)
+        if len(outs) != len(linears):
+            raise ValueError("one output per layer")
+        for o, lin in zip(outs, linears):
+            _require(o, (torch.bfloat16,), "out")
+            if o.numel() != m * lin.n:
+                raise ValueError("an output has the wrong size")
+    if m == 0:  # nothing to compute (an empty tensor has no device address to pass)
+        return [o.reshape(*lead, lin.n) for o, lin in zip(outs, linears)]
+    g = len(linears)
+    plans = (ctypes.c_void_p * g)(*[lin._plan.value for lin in linears])
+    optrs = (ctypes.c_void_p * g)(*[o.data_ptr() for o in outs])
+    check(lib().fp8_linear_run_group(ctypes.cast(plans, ctypes.c_void_p), g, m, _ptr(x2), kind,
+                                     _ptr(x_scale) if fp8_in else None, ctypes.cast(optrs, ctypes.c_void_p),
+                                     _ptr(ws), ws_bytes if ws is None else ws.numel(), _stream(x2)),
+          "fp8_linear_run_group")
+    return [o.reshape(*lead, lin.n) for o, lin in zip(outs, linears)]
 
 
 class Fp8WeightOnlyLinear:
@@ -407,5 +467,5 @@ def quant_gemm(a, w_fp8, w_scale, bias=None, out=None, workspace=None):
     return out, codes, scales
 
 
-__all__ = ["quant_rows", "quant_weights_per_channel", "Fp8Linear", "linear", "gemm_config_count",
+__all__ = ["quant_rows", "quant_weights_per_channel", "Fp8Linear", "linear", "linear_group", "gemm_config_count",
            "gemm_run_config", "quant_gemm", "A_BF16", "A_E4M3", "_lib"]

@@ -214,6 +214,30 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
                    void* stream);
 
 /*
+ * fp8_linear_run_group - several linears on one activation: the same results as
+ * nplans calls of fp8_linear_run(plans[i], m, a, a_kind, a_scale, outs_bf16[i], ...),
+ * with the activation quantised once (FP8W8A8_A_BF16). The retrospective (section 3.4)
+ * has the hidden states feed the Q, K and V projections (three weights, one input);
+ * quantising them once per token serves all three. When every plan would run
+ * the persistent GEMM configuration (6) at this m, the GEMMs go out as ONE launch
+ * whose workgroups walk the tiles of all the problems (one first prologue and one
+ * final output drain instead of nplans of each); otherwise each plan's GEMM runs as
+ * in fp8_linear_run. Outputs are bit-identical to the separate calls either way.
+ *
+ *   plans       1 <= nplans <= FP8W8A8_MAX_GROUP plans, all with the same k and device
+ *   outs_bf16   nplans device pointers, bf16 [m, n_i] each, 16-byte aligned
+ *   workspace   as fp8_linear_run, sized by fp8_linear_workspace_bytes(plans[0], m)
+ *   m, a, a_kind, a_scale, stream   as fp8_linear_run
+ * Returns FP8W8A8_ERR_INVALID_ARG for a NULL array or element or an nplans outside
+ * the range, FP8W8A8_ERR_BAD_SHAPE for plans whose k differ, FP8W8A8_ERR_BAD_DEVICE
+ * for plans on different devices; nothing is launched then.
+ */
+#define FP8W8A8_MAX_GROUP 4
+int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_t m, const void* a, int a_kind,
+                         const float* a_scale, void* const* outs_bf16, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * fp8_linear_run_noalloc - fp8_linear_run without a workspace argument, for callers
  * that cannot allocate device memory at all (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc). A FP8W8A8_A_BF16 run quantises the

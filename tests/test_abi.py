@@ -239,3 +239,30 @@ def test_noalloc_run_validation(lib):
     assert _lib.NOALLOC_SCRATCH_BYTES == 80 << 20
     assert lib.fp8_linear_run_noalloc(None, 4, A, _lib.A_BF16, None, A, None) == _lib.ERR_INVALID_ARG
     assert lib.fp8_linear_run_noalloc(None, 4, A, _lib.A_E4M3, A, A, None) == _lib.ERR_INVALID_ARG
+
+
+def test_run_group_validation(lib):
+    """The group entry point rejects NULL arrays, NULL elements and a group size outside
+    1..FP8W8A8_MAX_GROUP before it reads any plan."""
+    A = ALIGNED
+    assert re.search(r"#define FP8W8A8_MAX_GROUP (\d+)", open(HEADER).read()).group(1) == str(_lib.MAX_GROUP)
+    g = lib.fp8_linear_run_group
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    outs = (ctypes.c_void_p * 2)(A, A)
+    arr = lambda x: ctypes.cast(x, ctypes.c_void_p)  # noqa: E731
+    assert g(None, 1, 4, A, _lib.A_BF16, None, arr(outs), A, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert g(arr(nulls), 2, 4, A, _lib.A_BF16, None, None, A, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert g(arr(nulls), 2, 4, None, _lib.A_BF16, None, arr(outs), A, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert g(arr(nulls), 2, 4, A, _lib.A_BF16, None, arr(outs), A, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    five = (ctypes.c_void_p * 5)(A, A, A, A, A)
+    for n in (0, -1, _lib.MAX_GROUP + 1):
+        assert g(arr(five), n, 4, A, _lib.A_BF16, None, arr(five), A, 1 << 20, None) == _lib.ERR_INVALID_ARG, n
+
+
+def test_group_binding_rejects_bad_groups():
+    from fp8_w8a8_quantized_token_amd import linear_group
+
+    with pytest.raises(ValueError):
+        linear_group([], None)
+    with pytest.raises(ValueError):
+        linear_group([object()] * (_lib.MAX_GROUP + 1), None)
