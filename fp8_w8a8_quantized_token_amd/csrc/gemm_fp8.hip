@@ -64,6 +64,12 @@ namespace {
 // The persistent form runs up to kMaxGroup problems in one launch (see gemm_fp8_kernel).
 constexpr int kMaxGroup = FP8W8A8_MAX_GROUP;
 
+// Kernel forms by how workgroups map to tiles: one tile each; persistent over one
+// problem (the launch's own weight and output); persistent over a group of problems.
+// The single-problem persistent form is its own instantiation: finding a tile's problem
+// costs a dependent scalar load at every tile, measurable (about 1 %) on its own.
+constexpr int kPersistNone = 0, kPersistOne = 1, kPersistGroup = 2;
+
 struct GemmArgs {
   const uint8_t* qa;
   const float* a_scale;
@@ -80,9 +86,9 @@ struct GemmArgs {
   unsigned long long* flags;
   unsigned long long epoch;
   int shares, rows_per_share;
-  // persistent form: problems 0 .. ngroup - 1 share qa, a_scale, m and k; problem p has its
-  // own weight, w_scale, bias, output and n, and owns the global tile columns
-  // [g_tn_end[p - 1], g_tn_end[p]) (from 0 for p = 0). One problem when ungrouped.
+  // grouped persistent form: problems 0 .. ngroup - 1 share qa, a_scale, m and k; problem p
+  // has its own weight, w_scale, bias, output and n, and owns the global tile columns
+  // [g_tn_end[p - 1], g_tn_end[p]) (from 0 for p = 0). Unused by the other forms.
   int ngroup;
   int g_tn_end[kMaxGroup];
   int g_n[kMaxGroup];
@@ -132,8 +138,9 @@ struct TileProblem {
   uint16_t* out;
   int n, n0;
 };
-template <int BN>
+template <int BN, bool GROUPED>
 __device__ __forceinline__ TileProblem tile_problem(KernargGemmArgs k, int tn) {
+  if constexpr (!GROUPED) return TileProblem{k->qw, k->w_scale, k->bias, k->out, k->n, tn * BN};
   int p = 0, first = 0;
 #pragma unroll
   for (int i = 0; i + 1 < kMaxGroup; ++i)
@@ -252,7 +259,7 @@ __device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int
   __syncthreads();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED, bool PERSIST>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED, int PERSIST>
 struct KernelTag {};
 
 // FUSED: the single-launch form. The activation codes and scales do not exist yet at
@@ -269,7 +276,7 @@ struct KernelTag {};
 // wave, so that the wait for the next tile's stages (older than the stores) is an exact
 // count.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false,
-          bool PERSIST = false>
+          int PERSIST = kPersistNone>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
   using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED, PERSIST>;
   static_assert(BK == 64 || BK == 128, "stage depth in k bytes");
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   int n_cur = args.n;
   int n0 = tn * BN;
   if constexpr (PERSIST) {
-    const TileProblem pr = tile_problem<BN>(kernarg_args(), tn);
+    const TileProblem pr = tile_problem<BN, PERSIST == kPersistGroup>(kernarg_args(), tn);
     w_base = pr.qw;
     ws_base = pr.ws;
     b_base = pr.bias;
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     // Every wave has read the ring and this tile's epilogue operands (barrier above).
     // (args.shares holds the persistent grid size)
     const GemmArgs ra = reload_args();
-    const TileProblem cur = tile_problem<BN>(kernarg_args(), tn);  // this tile's output
+    const TileProblem cur = tile_problem<BN, PERSIST == kPersistGroup>(kernarg_args(), tn);  // this tile's output
     const int er0 = m0 + wm * WTM, ec0 = cur.n0 + wn * WTN;
     const int nt = ra.tiles_m * ra.tiles_n;
     vtile += ra.shares;
@@ -742,7 +749,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
       tile_coords_at<GROUP_M>(vtile, nt, ra.tiles_m, ra.tiles_n, tm, tn);
       tm = __builtin_amdgcn_readfirstlane(tm);
       tn = __builtin_amdgcn_readfirstlane(tn);
-      const TileProblem nx = tile_problem<BN>(kernarg_args(), tn);
+      const TileProblem nx = tile_problem<BN, PERSIST == kPersistGroup>(kernarg_args(), tn);
       m0 = tm * BM;
       n0 = nx.n0;
       rows_a = min(BM, ra.m - m0);
@@ -793,7 +800,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
     block_barrier();
     {
       const KernargGemmArgs kb = kernarg_args();
-      const TileProblem nx = tile_problem<BN>(kb, tn);
+      const TileProblem nx = tile_problem<BN, PERSIST == kPersistGroup>(kb, tn);
       issue_epi(kb->a_scale, nx.ws, nx.bias, m0, n0, rows_a, rows_w);
     }
     first_tile = false;
@@ -810,23 +817,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
 // PERSIST: one workgroup per CU (the LDS of a 256 x 256 tile admits no second), the
 // count rounded down to a multiple of the XCD count so that each workgroup's later tiles
 // stay on its own XCD; never more workgroups than tiles.
-template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false, bool PERSIST = false>
+template <int BM, int BN, int WM, int WN, int S, int BK, int GM, bool FUSED = false, int PERSIST = kPersistNone>
 hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
   GemmArgs args = a;
   args.tiles_m = (a.m + BM - 1) / BM;
   args.tiles_n = (a.n + BN - 1) / BN;
-  if (PERSIST) {
-    if (a.ngroup > 0) {
-      args.tiles_n = a.g_tn_end[a.ngroup - 1];  // the problems' tiles side by side
-    } else {  // one problem: the launch's own
-      args.ngroup = 1;
-      args.g_tn_end[0] = args.tiles_n;
-      args.g_n[0] = a.n;
-      args.g_qw[0] = a.qw;
-      args.g_ws[0] = a.w_scale;
-      args.g_bias[0] = a.bias;
-      args.g_out[0] = a.out;
-    }
+  if (PERSIST == kPersistGroup) {
+    if (a.ngroup < 1 || a.ngroup > kMaxGroup) return hipErrorInvalidValue;
+    args.tiles_n = a.g_tn_end[a.ngroup - 1];  // the problems' tiles side by side
   }
   const int64_t tiles = (int64_t)args.tiles_m * args.tiles_n;
   int64_t wgs = tiles;
@@ -1021,7 +1019,7 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 3: return launch<128, 128, 2, 2, 2, 128, 8>(a, stream);
     case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
     case 5: return launch_skinny<2>(a, stream);
-    case 6: return launch<256, 256, 2, 4, 2, 128, 4, false, true>(a, stream, cus);
+    case 6: return launch<256, 256, 2, 4, 2, 128, 4, false, kPersistOne>(a, stream, cus);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1042,7 +1040,7 @@ hipError_t launch_gemm_group(int64_t m, int64_t k, const uint8_t* qa, const floa
     a.g_bias[p] = probs[p].bias;
     a.g_out[p] = probs[p].out;
   }
-  return launch<256, 256, 2, 4, 2, 128, 4, false, true>(a, stream, cus);
+  return launch<256, 256, 2, 4, 2, 128, 4, false, kPersistGroup>(a, stream, cus);
 }
 
 hipError_t launch_quant_gemm(int64_t m, int64_t n, int64_t k, const uint16_t* a_bf16, uint8_t* qa_ws, float* sa_ws,
