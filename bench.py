@@ -422,37 +422,48 @@ def block_bench(torch, fp8, lib, dev, stream, steps, config):
 
 
 def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
-    """Per-tensor quantisation (both formats): two launches, HBM-resident rotating inputs."""
+    """Per-tensor quantisation (both formats), HBM-resident rotating inputs: the form
+    fp8_quant_tensor picks (one pass for e4m3fn up to 65536 elements per CU, else two
+    passes), and at the shape that fits one pass the other form beside it."""
     from fp8_w8a8_quantized_token_amd import _lib
     from workloads.synth import activation
     sptr = ctypes.c_void_p(stream.cuda_stream)
     ws = torch.empty((lib.fp8_quant_tensor_workspace_bytes(),), dtype=torch.uint8, device=dev)
     scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     out = {"bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s", "shapes": []}
     for rows, cols, nsets in ((8192, 2048, 16), (32760, 8192, 2)):
         xs = [activation(0, 5, 80 + i, rows, cols, "normal").to(dev) for i in range(nsets)]
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        fits = rows * cols <= 65536 * cus
         for fmt_name, fmt in (("e4m3fn", _lib.FMT_E4M3FN), ("e5m2", _lib.FMT_E5M2)):
-            def run(i):
-                st = lib.fp8_quant_tensor(ctypes.c_void_p(xs[i % nsets].data_ptr()), rows * cols, fmt,
-                                          ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(scale.data_ptr()),
-                                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr)
-                if st:
-                    raise _lib.Fp8W8A8Error(st, "fp8_quant_tensor")
-            preheat(torch, run)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for i in range(steps):
-                run(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / steps
+            one_pass = fits and fmt == _lib.FMT_E4M3FN  # what fp8_quant_tensor picks
+            def timed(form):
+                def run(i):
+                    st = lib.fp8_quant_tensor_form(form, ctypes.c_void_p(xs[i % nsets].data_ptr()), rows * cols, fmt,
+                                                   ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(scale.data_ptr()),
+                                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr)
+                    if st:
+                        raise _lib.Fp8W8A8Error(st, "fp8_quant_tensor_form")
+                preheat(torch, run)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(steps):
+                    run(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / steps
+            us = timed(_lib.TENSOR_FORMS["auto"])
             algo = 3 * rows * cols + 4
-            out["shapes"].append({"rows": rows, "cols": cols, "format": fmt_name, "us": round(us, 2),
-                                  "algorithmic_bytes": algo, "achieved": round(algo / (us * 1e-6) / 1e9, 1),
-                                  "hbm_bytes_two_pass": 5 * rows * cols + 4,
-                                  "frac": round(algo / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+            rec = {"rows": rows, "cols": cols, "format": fmt_name, "form": "one_pass" if one_pass else "two_pass",
+                   "us": round(us, 2), "algorithmic_bytes": algo, "achieved": round(algo / (us * 1e-6) / 1e9, 1),
+                   "hbm_bytes_of_form": (3 if one_pass else 5) * rows * cols + 4,
+                   "frac": round(algo / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+            if fits:  # the other form, for comparison
+                other = "two_pass" if one_pass else "one_pass"
+                rec[other + "_us"] = round(timed(_lib.TENSOR_FORMS[other]), 2)
+            out["shapes"].append(rec)
         del xs, q
         torch.cuda.empty_cache()
     return out

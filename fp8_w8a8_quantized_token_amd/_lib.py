@@ -32,6 +32,8 @@ ACT_TABLE_BYTES = 131072
 FMT_E4M3FN = 0
 FMT_E5M2 = 1
 
+TENSOR_FORMS = {"auto": 0, "one_pass": 1, "two_pass": 2, "one_pass_no_wait": 3}
+
 NOALLOC_SCRATCH_BYTES = 80 << 20
 
 MAX_ROWS = 1 << 24
@@ -49,6 +51,8 @@ SIGNATURES = {
     "fp8_act_table_build": (ctypes.c_int, [ctypes.c_int, _c_p, _c_p]),
     "fp8_quant_tensor_workspace_bytes": (ctypes.c_size_t, []),
     "fp8_quant_tensor": (ctypes.c_int, [_c_p, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "fp8_quant_tensor_form": (ctypes.c_int, [ctypes.c_int, _c_p, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p,
+                                             ctypes.c_size_t, _c_p]),
     "fp8_dequant_tensor": (ctypes.c_int, [_c_p, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p]),
     "fp8_act_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "fp8_act_quant_rows": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),

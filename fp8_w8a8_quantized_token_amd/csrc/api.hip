@@ -365,8 +365,9 @@ static int check_tensor_args(const void* x, int64_t numel, int format, const voi
   return FP8W8A8_OK;
 }
 
-int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int fp8_quant_tensor_form(int form, const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (form < FP8W8A8_TENSOR_FORM_AUTO || form > FP8W8A8_TENSOR_FORM_ONE_PASS_NO_WAIT) return FP8W8A8_ERR_INVALID_ARG;
   int st = check_tensor_args(x_bf16, numel, format, q_out);
   if (st != FP8W8A8_OK) return st;
   if (!scale_out || !workspace) return FP8W8A8_ERR_INVALID_ARG;
@@ -376,9 +377,23 @@ int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out,
   int cus = 0;
   st = current_device_ok(&cus);
   if (st != FP8W8A8_OK) return st;
+  if ((form == FP8W8A8_TENSOR_FORM_ONE_PASS || form == FP8W8A8_TENSOR_FORM_ONE_PASS_NO_WAIT) &&
+      !quant_tensor_fits_one_pass(numel, cus))
+    return FP8W8A8_ERR_BAD_SHAPE;
+  static_assert(kTensorAuto == FP8W8A8_TENSOR_FORM_AUTO && kTensorOnePass == FP8W8A8_TENSOR_FORM_ONE_PASS &&
+                    kTensorTwoPass == FP8W8A8_TENSOR_FORM_TWO_PASS &&
+                    kTensorOnePassNoWait == FP8W8A8_TENSOR_FORM_ONE_PASS_NO_WAIT,
+                "form numbering");
   hipError_t e = launch_quant_tensor(static_cast<const uint16_t*>(x_bf16), numel, format, static_cast<uint8_t*>(q_out),
-                                     scale_out, static_cast<float*>(workspace), cus, static_cast<hipStream_t>(stream));
+                                     scale_out, static_cast<float*>(workspace), cus, static_cast<hipStream_t>(stream),
+                                     form);
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
+}
+
+int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return fp8_quant_tensor_form(FP8W8A8_TENSOR_FORM_AUTO, x_bf16, numel, format, q_out, scale_out, workspace,
+                               workspace_bytes, stream);
 }
 
 int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* scale, float* out_f32, void* stream) {

@@ -24,11 +24,15 @@ hipError_t launch_act_rows(const uint16_t* x, int64_t elems, const uint16_t* tab
 hipError_t launch_act_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* table, uint8_t* q,
                                  float* scale, int cus, hipStream_t stream);
 
-// Per-tensor quantisation (amax partials into `workspace`, then the codes and the scale)
-// and fp32 dequantisation; numel % 16 == 0, 16-byte aligned buffers.
+// Per-tensor quantisation (per-workgroup maxima into `workspace`, then the codes and the
+// scale) and fp32 dequantisation; numel % 16 == 0, 16-byte aligned buffers. form: one of
+// kTensor* (FP8W8A8_TENSOR_FORM_*); a one-pass form on a tensor that does not fit gives
+// hipErrorInvalidValue.
+constexpr int kTensorAuto = 0, kTensorOnePass = 1, kTensorTwoPass = 2, kTensorOnePassNoWait = 3;
 size_t quant_tensor_workspace_bytes();
+bool quant_tensor_fits_one_pass(int64_t numel, int cus);
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t numel, int fmt, uint8_t* q, float* scale, float* workspace,
-                               int cus, hipStream_t stream);
+                               int cus, hipStream_t stream, int form = kTensorAuto);
 hipError_t launch_dequant_tensor(const uint8_t* q, int64_t numel, int fmt, const float* scale, float* out, int cus,
                                  hipStream_t stream);
 

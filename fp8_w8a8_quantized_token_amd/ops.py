@@ -123,14 +123,18 @@ def act_quant_rows(x, table, q=None, scale=None):
 FORMATS = {"e4m3fn": FMT_E4M3FN, "e5m2": FMT_E5M2}
 
 
-def quant_tensor(x, fmt="e4m3fn", workspace=None):
+def quant_tensor(x, fmt="e4m3fn", workspace=None, form="auto"):
     """Per-tensor quantisation of a bf16 tensor -> (codes uint8 of x's shape, scale fp32 [1]).
 
     One scale for the whole tensor, s = amax / fmax (448 for e4m3fn, 57344 for e5m2):
     the state-dict conversion of the QuantizeFP8Format page. numel must be a multiple of 16.
+    ``form`` picks the kernel form ("auto", "one_pass", "two_pass", "one_pass_no_wait";
+    include/fp8w8a8.h, fp8_quant_tensor_form); every form gives the same result.
     """
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
+    if form not in _lib.TENSOR_FORMS:
+        raise ValueError(f"unknown form {form!r}; expected one of {sorted(_lib.TENSOR_FORMS)}")
     xc = x.contiguous()
     _require(xc, (torch.bfloat16,), "x")
     q = torch.empty(xc.shape, dtype=torch.uint8, device=xc.device)
@@ -138,8 +142,9 @@ def quant_tensor(x, fmt="e4m3fn", workspace=None):
     ws_bytes = lib().fp8_quant_tensor_workspace_bytes()
     if workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=xc.device)
-    check(lib().fp8_quant_tensor(_ptr(xc), xc.numel(), FORMATS[fmt], _ptr(q), _ptr(s), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(xc)), "fp8_quant_tensor")
+    check(lib().fp8_quant_tensor_form(_lib.TENSOR_FORMS[form], _ptr(xc), xc.numel(), FORMATS[fmt], _ptr(q), _ptr(s),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(xc)),
+          "fp8_quant_tensor_form")
     return q, s
 
 

@@ -359,8 +359,13 @@ int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const vo
  *   q_out      device, u8 codes [numel], 16-byte aligned, written
  *   scale_out  device, one fp32, 4-byte aligned, written
  *   workspace  device, fp8_quant_tensor_workspace_bytes() bytes, 16-byte aligned, scratch
- *              (per-workgroup maxima); its contents need no initialisation
- * Two launches on `stream`. Inputs must be finite.
+ *              (per-workgroup maxima); its contents need no initialisation; two
+ *              calls that overlap in time must not share it
+ * Two launches on `stream`. Inputs must be finite. An e4m3fn tensor that fits in the
+ * registers of one workgroup per compute unit (numel <= 65536 x CUs: 16.8 M elements,
+ * 32 MiB of bf16, on 256 CUs) is read once: a small launch marks the maxima unwritten,
+ * then the workgroups hold their shares, publish their maxima, wait for the largest
+ * and quantise what they hold. Other tensors are read twice (maxima, then codes).
  */
 #define FP8W8A8_FMT_E4M3FN 0
 #define FP8W8A8_FMT_E5M2 1
@@ -368,6 +373,23 @@ int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const vo
 size_t fp8_quant_tensor_workspace_bytes(void);
 int fp8_quant_tensor(const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_quant_tensor_form - fp8_quant_tensor with its form chosen, a test and measurement
+ * hook: FP8W8A8_TENSOR_FORM_AUTO (what fp8_quant_tensor does), _ONE_PASS (returns
+ * FP8W8A8_ERR_BAD_SHAPE, launching nothing, for a tensor that does not fit), _TWO_PASS,
+ * or _ONE_PASS_NO_WAIT: one pass in which no workgroup waits for the others; each reads
+ * the whole input for the maximum itself (the path a workgroup takes if the others have
+ * not arrived within 1 ms, e.g. while another stream's kernel holds CUs). Codes and
+ * scale are identical in every form. Other arguments and statuses as fp8_quant_tensor;
+ * an unknown form is FP8W8A8_ERR_INVALID_ARG.
+ */
+#define FP8W8A8_TENSOR_FORM_AUTO 0
+#define FP8W8A8_TENSOR_FORM_ONE_PASS 1
+#define FP8W8A8_TENSOR_FORM_TWO_PASS 2
+#define FP8W8A8_TENSOR_FORM_ONE_PASS_NO_WAIT 3
+int fp8_quant_tensor_form(int form, const void* x_bf16, int64_t numel, int format, void* q_out, float* scale_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* out_f32[i] = fl32(dec(q[i]) * *scale). q 16-byte aligned, out_f32 16-byte aligned, scale device fp32. */
 int fp8_dequant_tensor(const void* q, int64_t numel, int format, const float* scale, float* out_f32, void* stream);

@@ -266,3 +266,14 @@ def test_group_binding_rejects_bad_groups():
         linear_group([], None)
     with pytest.raises(ValueError):
         linear_group([object()] * (_lib.MAX_GROUP + 1), None)
+
+
+def test_quant_tensor_form_validation(lib):
+    A = ALIGNED
+    f = lib.fp8_quant_tensor_form
+    for form in (-1, 4, 99):
+        assert f(form, A, 16, 0, A, A, A, 4096, None) == _lib.ERR_INVALID_ARG, form
+    for form in _lib.TENSOR_FORMS.values():
+        assert f(form, A, 20, 0, A, A, A, 4096, None) == _lib.ERR_BAD_SHAPE, form
+        assert f(form, A, 0, 0, A, A, A, 4096, None) == _lib.OK, form  # empty: a no-op
+    assert re.search(r"#define FP8W8A8_TENSOR_FORM_ONE_PASS_NO_WAIT (\d+)", open(HEADER).read()).group(1) == "3"

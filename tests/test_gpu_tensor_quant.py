@@ -2,8 +2,11 @@
 
 Codes, the scale and the dequantised values are integer / byte results once the
 precision is fixed, so every comparison with the oracle is bit for bit. Covered:
-random tensors of several sizes (one 16-element group, ragged grid-stride tails, a
-weight-sized tensor) in both formats; every finite bf16 value through each format's
+random tensors of several sizes in both formats, on both kernel forms (one pass: one
+16-element group, ragged partial grids, one to four groups per thread, the largest tensor
+that fits; two passes: just above it), every form on the same tensors (the one-pass form
+also with no workgroup waiting for the others), the maximum held by the first or the last
+workgroup only; every finite bf16 value through each format's
 conversion (a tensor whose amax equals the format's largest value has scale 1, so
 the quotients are the values themselves); zero tensors; tensors whose scale is an
 fp32 subnormal (the exact-division path), down to the smallest bf16 amax values, whose
@@ -28,8 +31,8 @@ def _gpu(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def _check(bits, fmt, dev):
-    q, s = fp8.quant_tensor(_gpu(bits, dev), fmt)
+def _check(bits, fmt, dev, form="auto"):
+    q, s = fp8.quant_tensor(_gpu(bits, dev), fmt, form=form)
     eq, es = otq.quant_tensor(bits, fmt)
     assert np.array_equal(q.cpu().numpy().reshape(eq.shape), eq), fmt
     assert s.cpu().numpy().view(np.uint32)[0] == np.float32(es).view(np.uint32), fmt
@@ -38,13 +41,59 @@ def _check(bits, fmt, dev):
     assert np.array_equal(d.cpu().numpy().reshape(ed.shape).view(np.uint32), ed.view(np.uint32)), fmt
 
 
+# one pass: one group, ragged partial grids, one group per thread on every CU, two and
+# four groups per thread (ragged), the largest one-pass tensor on 256 CUs; two passes: just
+# above it
+SHAPES = [(16,), (1008,), (37, 272), (2048, 2048), (3000, 2048), (8192, 2048), (8200, 2048)]
+
+
+def _random_bits(shape, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * np.exp2(rng.integers(-8, 8))).astype(np.float32)
+    return bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("shape", [(16,), (1008,), (37, 272), (8192, 2048)])
+@pytest.mark.parametrize("shape", SHAPES)
 def test_random_tensors(fmt, shape):
     dev = require_gpu()
-    rng = np.random.default_rng(sum(shape))
-    x = (rng.standard_normal(shape) * np.exp2(rng.integers(-8, 8))).astype(np.float32)
-    _check(bf16_bits(torch.from_numpy(x).to(torch.bfloat16)), fmt, dev)
+    _check(_random_bits(shape, sum(shape)), fmt, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("form", ["one_pass", "two_pass", "one_pass_no_wait"])
+@pytest.mark.parametrize("shape", [(37, 272), (3000, 2048), (8192, 2048)])
+def test_every_form_on_the_same_tensors(fmt, form, shape):
+    # one_pass_no_wait: every workgroup computes the maximum over the whole input itself,
+    # the path a workgroup takes when the others do not arrive in time
+    dev = require_gpu()
+    _check(_random_bits(shape, 7 + sum(shape)), fmt, dev, form=form)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_maximum_in_one_workgroup_only(fmt, where):
+    # the scale depends on one element held by the first or the last workgroup
+    dev = require_gpu()
+    bits = _random_bits((3000, 2048), 11).copy()
+    big = np.uint16(0x4580)  # bf16 4096, above every other magnitude here
+    if where == "first":
+        bits.reshape(-1)[5] = big
+    else:
+        bits.reshape(-1)[-3] = big | np.uint16(0x8000)
+    _check(bits, fmt, dev)
+
+
+def test_one_pass_refuses_a_tensor_that_does_not_fit():
+    dev = require_gpu()
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the one-pass capacity is 65536 elements per CU; sized for 256 CUs")
+    x = torch.zeros((8200, 2048), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(fp8.Fp8W8A8Error, match="shape"):
+        fp8.quant_tensor(x, "e4m3fn", form="one_pass")
+    q, s = fp8.quant_tensor(x, "e4m3fn", form="two_pass")
+    torch.cuda.synchronize()
+    assert float(s) == 0.0 and int(q.view(torch.uint8).max()) == 0
 
 
 @pytest.mark.parametrize("fmt", FMTS)
