@@ -400,19 +400,27 @@ def block_bench(torch, fp8, lib, dev, stream, steps, config):
                     if st:
                         raise _lib.Fp8W8A8Error(st, "fp8_linear_run")
 
-        preheat(torch, step, batch=5)
+        return step
+
+    steps_of = {False: run(False), True: run(True)}
+    for fn in steps_of.values():
+        preheat(torch, fn, batch=5)
+    # the two forms alternate (5 rounds each, median): one run of each after the other
+    # differed by +-2% from order and clock alone
+    times = {False: [], True: []}
+    for rnd in range(10):
+        grouped = (rnd % 2 == 1) if (rnd // 2) % 2 == 0 else (rnd % 2 == 0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(steps):
-            step(i)
+            steps_of[grouped](i)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    ms_sep = run(False)
-    ms = run(True)
-    res = {"quantisations": len(order), "gemms": len(lins), "steps": steps, "flop_per_step": flop,
+        times[grouped].append(e0.elapsed_time(e1) / steps)
+    ms_sep = sorted(times[False])[2]
+    ms = sorted(times[True])[2]
+    res = {"quantisations": len(order), "gemms": len(lins), "steps": steps, "rounds": 5, "flop_per_step": flop,
            "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
            "grouped": True, "ms_per_step_separate_gemms": round(ms_sep, 4),
            "gemm_configs": {layer: lin.config(outs[layer].shape[0])[0] for layer, lin in lins.items()}}
