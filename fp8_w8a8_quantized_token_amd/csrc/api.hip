@@ -510,13 +510,20 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
   if (m == 0) return FP8W8A8_OK;
   int st = plan_device_current(p0->device);
   if (st != FP8W8A8_OK) return st;
-  // every plan's choice at this m; one launch when all of them take the persistent form
+  // every plan's choice at this m; one launch when all of them take the persistent form,
+  // or all the skinny one
   int config[FP8W8A8_MAX_GROUP];
-  bool grouped = nplans > 1;
   for (int i = 0; i < nplans; ++i) {
     config[i] = plan_bucket_config(plans[i], m);
     if (!grid_fits(config[i], m, plans[i]->n)) return FP8W8A8_ERR_BAD_SHAPE;
-    if (config[i] != kW8A8Persistent) grouped = false;
+  }
+  bool grouped = nplans > 1 && (config[0] == kW8A8Persistent || config[0] == kW8A8Skinny);
+  for (int i = 1; i < nplans; ++i)
+    if (config[i] != config[0]) grouped = false;
+  if (grouped && config[0] == kW8A8Skinny) {  // the joint grid must fit as each plan's does
+    int64_t wgs = 0;
+    for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);
+    if (wgs * gemm_threads(kW8A8Skinny) >= kMaxGridThreads) grouped = false;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* qa = static_cast<const uint8_t*>(a);
@@ -534,8 +541,9 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
     for (int i = 0; i < nplans; ++i)
       probs[i] = GroupProblem{plans[i]->w, plans[i]->w_scale, plans[i]->bias, static_cast<uint16_t*>(outs_bf16[i]),
                               plans[i]->n};
-    return launch_gemm_group(m, p0->k, qa, sa, nplans, probs, p0->cu_count, s) == hipSuccess ? FP8W8A8_OK
-                                                                                            : FP8W8A8_ERR_HIP;
+    return launch_gemm_group(config[0], m, p0->k, qa, sa, nplans, probs, p0->cu_count, s) == hipSuccess
+               ? FP8W8A8_OK
+               : FP8W8A8_ERR_HIP;
   }
   for (int i = 0; i < nplans; ++i) {
     const fp8_linear_plan* p = plans[i];

@@ -873,22 +873,25 @@ struct SkinnyFrags {
   v8i a[kSkinnyBatch][MT];
 };
 
-template <int MT>
+// GROUPED: the problems of GemmArgs' group side by side along the workgroups' column
+// blocks (g_tn_end counts 16-channel blocks here); each workgroup looks its problem up.
+template <int MT, bool GROUPED = false>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs args) {
   constexpr int WAVES = kSkinnyWaves;
   constexpr int TM = 16 * MT;  // tokens per workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tn = blockIdx.x % args.tiles_n, tm = blockIdx.x / args.tiles_n;
-  const int n0 = tn * kSkinnyNW, m0 = tm * TM;
+  const TileProblem pr = tile_problem<kSkinnyNW, GROUPED>(kernarg_args(), tn);
+  const int n = pr.n, n0 = pr.n0, m0 = tm * TM;
   const int K = args.k;
   const int rows_a = min(TM, args.m - m0);
-  const int rows_w = min(kSkinnyNW, args.n - n0);
+  const int rows_w = min(kSkinnyNW, n - n0);
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qa) + (int64_t)m0 * K, 0,
                                         (uint32_t)rows_a * (uint32_t)K, kBufferConfig);
   const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qw) + (int64_t)n0 * K, 0,
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pr.qw) + (int64_t)n0 * K, 0,
                                         (uint32_t)rows_w * (uint32_t)K, kBufferConfig);
 
   // epilogue operands of this thread's output (token t / 16, channel t % 16: every output of
@@ -899,8 +902,8 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
   float e_sa = 0.0f, e_sw = 0.0f, e_b = 0.0f;
   if (evalid) {
     e_sa = args.a_scale[m0 + et];
-    e_sw = args.w_scale[n0 + ec];
-    if (args.bias) e_b = __uint_as_float((uint32_t)args.bias[n0 + ec] << 16);
+    e_sw = pr.ws[n0 + ec];
+    if (pr.bias) e_b = __uint_as_float((uint32_t)pr.bias[n0 + ec] << 16);
   }
 
   const int r = lane & 15, q = lane >> 4;
@@ -965,17 +968,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
   for (int w = 0; w < WAVES; ++w) sum += red[w][et >> 4][src_lane][ec & 3];
   if (evalid) {
     const float v = __builtin_fmaf(sum * e_sa, e_sw, e_b);
-    args.out[(int64_t)(m0 + et) * args.n + n0 + ec] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    pr.out[(int64_t)(m0 + et) * n + n0 + ec] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
   }
 }
 
-template <int MT>
+template <int MT, bool GROUPED = false>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
   GemmArgs args = a;
-  args.tiles_n = (a.n + kSkinnyNW - 1) / kSkinnyNW;
+  if (GROUPED && (a.ngroup < 1 || a.ngroup > kMaxGroup)) return hipErrorInvalidValue;
+  args.tiles_n = GROUPED ? a.g_tn_end[a.ngroup - 1] : (a.n + kSkinnyNW - 1) / kSkinnyNW;
   args.tiles_m = (a.m + 16 * MT - 1) / (16 * MT);
   const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_skinny<MT><<<dim3((unsigned)wgs), dim3(kSkinnyWaves * 64), 0, stream>>>(args);
+  gemm_fp8_skinny<MT, GROUPED><<<dim3((unsigned)wgs), dim3(kSkinnyWaves * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -1024,15 +1028,17 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
   }
 }
 
-hipError_t launch_gemm_group(int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
+hipError_t launch_gemm_group(int id, int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
                              const GroupProblem* probs, int cus, hipStream_t stream) {
   if (nprob < 1 || nprob > kMaxGroup) return hipErrorInvalidValue;
+  if (id != 5 && id != 6) return hipErrorInvalidValue;
   GemmArgs a{qa, a_scale, probs[0].qw, probs[0].w_scale, probs[0].bias, probs[0].out, (int)m, (int)probs[0].n,
              (int)k, 0, 0};
   a.ngroup = nprob;
+  const int cols = id == 6 ? 256 : kSkinnyNW;  // the form's column block
   int tn = 0;
   for (int p = 0; p < nprob; ++p) {
-    tn += (int)((probs[p].n + 255) / 256);  // the persistent form's 256-column tiles
+    tn += (int)((probs[p].n + cols - 1) / cols);
     a.g_tn_end[p] = tn;
     a.g_n[p] = (int)probs[p].n;
     a.g_qw[p] = probs[p].qw;
@@ -1040,6 +1046,7 @@ hipError_t launch_gemm_group(int64_t m, int64_t k, const uint8_t* qa, const floa
     a.g_bias[p] = probs[p].bias;
     a.g_out[p] = probs[p].out;
   }
+  if (id == 5) return launch_skinny<2, true>(a, stream);
   return launch<256, 256, 2, 4, 2, 128, 4, false, kPersistGroup>(a, stream, cus);
 }
 

@@ -59,9 +59,9 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
                        const uint8_t* qw, const float* w_scale, const uint16_t* bias, uint16_t* out, int cus,
                        hipStream_t stream);
 
-// The persistent configuration over up to FP8W8A8_MAX_GROUP problems that share the
-// activation codes qa [m, k] and scales: problem p is out_p[m, n_p] = epilogue(qa x
-// qw_p^T), all in one launch (one workgroup per CU walking the problems' tiles).
+// Configuration `id` (6, persistent; or 5, skinny) over up to FP8W8A8_MAX_GROUP problems
+// that share the activation codes qa [m, k] and scales: problem p is out_p[m, n_p] =
+// epilogue(qa x qw_p^T), all in one launch (the problems' column blocks side by side).
 struct GroupProblem {
   const uint8_t* qw;
   const float* w_scale;
@@ -69,7 +69,7 @@ struct GroupProblem {
   uint16_t* out;
   int64_t n;
 };
-hipError_t launch_gemm_group(int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
+hipError_t launch_gemm_group(int id, int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
                              const GroupProblem* probs, int cus, hipStream_t stream);
 
 // Per-token quantisation and the FP8 GEMM (configuration 0) in one launch. qa_ws [m, k]

@@ -221,8 +221,11 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
  * quantising them once per token serves all three. When every plan would run
  * the persistent GEMM configuration (6) at this m, the GEMMs go out as ONE launch
  * whose workgroups walk the tiles of all the problems (one first prologue and one
- * final output drain instead of nplans of each); otherwise each plan's GEMM runs as
- * in fp8_linear_run. Outputs are bit-identical to the separate calls either way.
+ * final output drain instead of nplans of each); when every plan would run the skinny
+ * configuration (5, a few tokens), as ONE launch over all the problems' channel blocks
+ * (enough workgroups to fill the device, where one problem alone leaves it half idle);
+ * otherwise each plan's GEMM runs as in fp8_linear_run. Outputs are bit-identical to the
+ * separate calls either way.
  *
  *   plans       1 <= nplans <= FP8W8A8_MAX_GROUP plans, all with the same k and device
  *   outs_bf16   nplans device pointers, bf16 [m, n_i] each, 16-byte aligned

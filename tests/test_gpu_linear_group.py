@@ -2,14 +2,15 @@
 
 The retrospective (aigcage.com, section 3.4) feeds one set of hidden states into the
 Q, K and V projections. fp8_linear_run_group runs such a group: one per-token
-quantisation, then either ONE persistent GEMM launch over every problem's tiles (when
-each plan would take the persistent configuration at this m) or each plan's own GEMM.
+quantisation, then ONE GEMM launch over every problem's tiles when each plan would take
+the persistent configuration at this m (or each the skinny one, at a few tokens), else
+each plan's own GEMM.
 Each output must be bit-identical to the plan's separate fp8_linear_run (same codes,
 same products summed in the same order), and rows of it (the first tile row and the
 ragged last one) are compared with the float64 oracle under the linear tests' bound.
 Covered: groups of 1..4 problems with ragged n (a partial last tile column in each
-problem), with and without bias in one group, bf16 and e4m3fn inputs, groups that fall
-back to per-plan launches (few tokens, mixed configurations), m = 0, the C ABI's
+problem), with and without bias in one group, bf16 and e4m3fn inputs, skinny groups at
+1..32 tokens, groups that fall back to per-plan launches (mixed configurations), m = 0, the C ABI's
 shape and workspace checks, and the Q/K/V projections at full size.
 """
 
@@ -27,6 +28,7 @@ from workloads import bf16_bits, make_case, make_config
 pytestmark = pytest.mark.gpu
 
 PERSISTENT = 6
+SKINNY = 5
 
 
 def _cus(dev):
@@ -111,15 +113,40 @@ def test_groups_of_one_and_of_four():
     _check_rows_against_oracle(four, cases, qa, sa, "group of four")
 
 
-@pytest.mark.parametrize("m", [0, 1, 26, 700, 3000, 8200])
+@pytest.mark.parametrize("m", [1, 17, 26, 32])
+@pytest.mark.parametrize("a_kind", ["bf16", "e4m3"])
+def test_group_of_skinny_problems_in_one_launch(m, a_kind):
+    # a few tokens (the 26-row encoder input): every plan takes the skinny form, and the
+    # group runs as one launch over all the problems' 16-channel blocks
+    dev = require_gpu()
+    k = 2048
+    ns = (4112, 1040, 2064)
+    lins, cases = _layers(ns, k, dev, seed=51, no_bias=(1,))
+    assert all(lin.config(m)[0] == SKINNY for lin in lins)
+    a = make_case(m, 16, k, seed=52, kind="outlier").a
+    qa, sa = cref.quant_rows(bf16_bits(a))
+    if a_kind == "bf16":
+        x, xs = a.to(dev), None
+    else:
+        x, xs = torch.from_numpy(qa).to(dev), torch.from_numpy(sa).to(dev)
+    separate = [lin(x, xs) for lin in lins]
+    grouped = linear_group(lins, x, xs)
+    torch.cuda.synchronize()
+    for i, (g, s) in enumerate(zip(grouped, separate)):
+        assert torch.equal(_bits(g), _bits(s)), f"m={m} problem {i}"
+    _check_rows_against_oracle(grouped, cases, qa, sa, f"skinny group m={m}")
+
+
+@pytest.mark.parametrize("m", [0, 700, 3000, 8200])
 def test_group_falls_back_to_each_plans_own_launch(m):
-    # at these m at least one plan does not take the persistent form (few tokens, or a
-    # narrow weight next to a wide one): every plan runs its own GEMM on the shared codes
+    # at these m the plans do not all take one groupable form (a narrow weight next to a
+    # wide one, or neither persistent nor skinny): every plan runs its own GEMM on the
+    # shared codes
     dev = require_gpu()
     k = 2048
     lins, cases = _layers((4112, 1040), k, dev, seed=31)
     if m > 0 and _cus(dev) == 256:
-        assert lins[1].config(m)[0] != PERSISTENT
+        assert lins[1].config(m)[0] not in (PERSISTENT, SKINNY)
     a = make_case(max(m, 1), 16, k, seed=32, kind="outlier").a[:m]
     x = a.to(dev)
     separate = [lin(x) for lin in lins]
