@@ -6,7 +6,7 @@ random tensors of several sizes in both formats, on both kernel forms (one pass:
 16-element group, ragged partial grids, one to four groups per thread, the largest tensor
 that fits; two passes: just above it), every form on the same tensors (the one-pass form
 also with no workgroup waiting for the others), the maximum held by the first or the last
-workgroup only; every finite bf16 value through each format's
+workgroup only; both forms captured in a HIP graph and replayed with new inputs; every finite bf16 value through each format's
 conversion (a tensor whose amax equals the format's largest value has scale 1, so
 the quotients are the values themselves); zero tensors; tensors whose scale is an
 fp32 subnormal (the exact-division path), down to the smallest bf16 amax values, whose
@@ -159,3 +159,34 @@ def test_weight_quantised_per_tensor_feeds_nothing_else():
     q1, s1 = fp8.quant_tensor(case.w.to(dev), "e4m3fn")
     q2, s2 = fp8.quant_weights_per_channel(case.w.to(dev))
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("form", ["one_pass", "two_pass"])
+def test_graph_replays_with_new_inputs(form):
+    # both forms are two kernels with no memset: captured once, each replay (with a new
+    # input copied in between and eager work around it) must give that input's codes
+    dev = require_gpu()
+    shape = (3000, 2048)
+    x = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((fp8.lib().fp8_quant_tensor_workspace_bytes(),), dtype=torch.uint8, device=dev)
+    x.copy_(_gpu(_random_bits(shape, 100), dev))
+    fp8.quant_tensor(x, "e4m3fn", workspace=ws, form=form)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=side):
+        q, s = fp8.quant_tensor(x, "e4m3fn", workspace=ws, form=form)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        bits = _random_bits(shape, 101 + rep)
+        if rep == 2:
+            bits = bits.copy()
+            bits.reshape(-1)[-1] = np.uint16(0x4580)  # a new maximum, in the last workgroup
+        x.copy_(_gpu(bits, dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eq, es = otq.quant_tensor(bits, "e4m3fn")
+        assert s.cpu().numpy().view(np.uint32)[0] == np.float32(es).view(np.uint32), f"replay {rep}: scale"
+        assert np.array_equal(q.cpu().numpy().reshape(eq.shape), eq), f"replay {rep}: codes"
