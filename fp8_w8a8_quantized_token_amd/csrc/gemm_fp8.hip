@@ -52,6 +52,11 @@
 //     its tiles and requests the next tile's first two stages as soon as the current
 //     tile's k loop is done, so they land during its epilogue instead of after it. It
 //     computes exactly what configuration 0 computes, in the same order.
+//   * Groups (section 3.4 of the page: the hidden states feed the Q, K and V
+//     projections): up to kMaxGroup problems that share the activation codes run as one
+//     launch of the persistent or of the skinny form, their column blocks side by side;
+//     each tile looks up its problem's weight, scales, bias, output and width. Each tile
+//     computes what the problem's own launch computes, bit for bit.
 #include <algorithm>
 
 #include "internal.h"
