@@ -10,7 +10,8 @@ same products summed in the same order), and rows of it (the first tile row and 
 ragged last one) are compared with the float64 oracle under the linear tests' bound.
 Covered: groups of 1..4 problems with ragged n (a partial last tile column in each
 problem), with and without bias in one group, bf16 and e4m3fn inputs, skinny groups at
-1..32 tokens, groups that fall back to per-plan launches (mixed configurations), m = 0, the C ABI's
+1..32 tokens, groups that fall back to per-plan launches (mixed configurations), m = 0,
+a grouped call captured in a HIP graph and replayed with new inputs, the C ABI's
 shape and workspace checks, and the Q/K/V projections at full size.
 """
 
@@ -212,3 +213,37 @@ def test_qkv_group_full_size():
         assert_codes_equal(qx, sx, qa, sa, f"qkv/{act} codes")
         cases = [SimpleNamespace(w=cfg["weights"][n], bias=cfg["biases"][n]) for n in names]
         _check_rows_against_oracle(grouped, cases, qa, sa, f"qkv group {act}")
+
+
+@pytest.mark.parametrize("m", [26, 8200])
+def test_group_replayed_from_a_graph_with_new_inputs(m):
+    # one grouped call (quantisation + one GEMM launch, skinny at 26 tokens, persistent at
+    # 8200) captured once and replayed with new inputs copied in between; every replay must
+    # equal the eager separate runs on that input, bit for bit
+    dev = require_gpu()
+    k = 2048
+    lins, _ = _layers((4112, 4624), k, dev, seed=61, no_bias=(0,))
+    if _cus(dev) == 256:
+        assert len({lin.config(m)[0] for lin in lins}) == 1 and lins[0].config(m)[0] in (SKINNY, PERSISTENT)
+    inputs = [make_case(m, 16, k, seed=62 + i, kind="outlier").a.to(dev) for i in range(3)]
+    x = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((lins[0].workspace_bytes(m),), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((m, lin.n), dtype=torch.bfloat16, device=dev) for lin in lins]
+    x.copy_(inputs[0])
+    linear_group(lins, x, outs=outs, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(g, stream=side):
+        linear_group(lins, x, outs=outs, workspace=ws)
+    torch.cuda.synchronize()
+    for inp in inputs:
+        x.copy_(inp)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        expect = [lin(inp) for lin in lins]
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, expect)):
+            assert torch.equal(_bits(o), _bits(e)), f"m={m} problem {i}"
