@@ -264,7 +264,8 @@ __device__ __forceinline__ void await_shares(const GemmArgs& args, int wave, int
   __syncthreads();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED, int PERSIST>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED, int PERSIST,
+          bool W_FIRST>
 struct KernelTag {};
 
 // FUSED: the single-launch form. The activation codes and scales do not exist yet at
@@ -281,9 +282,9 @@ struct KernelTag {};
 // wave, so that the wait for the next tile's stages (older than the stores) is an exact
 // count.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int GROUP_M, bool FUSED = false,
-          int PERSIST = kPersistNone>
+          int PERSIST = kPersistNone, bool W_FIRST = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArgs args) {
-  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED, PERSIST>;
+  using Tag = KernelTag<BM, BN, WAVES_M, WAVES_N, STAGES, BK, GROUP_M, FUSED, PERSIST, W_FIRST>;
   static_assert(BK == 64 || BK == 128, "stage depth in k bytes");
   constexpr int H = BK / 64;         // 32x32x64 MFMA k-steps per stage
   constexpr int CPR = BK / 16;       // 16-byte chunks per tile row
@@ -324,6 +325,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
   // in two halves: the activation rows right after the stage barrier, the weight rows
   // one MFMA k-step later (they still land before the next barrier).
   constexpr bool kSplitRefill = STAGES == 2 && H == 2 && kFillWaves < kWaves;
+  // W_FIRST: the weight rows of a split refill go out at the stage barrier and the
+  // activation rows one k-step later (else the other way round). The launcher sends the
+  // operand with more bytes in all first: its slices are the likelier L2 misses and need
+  // the longer lead (FFN-up, n = 2 m: 65.8 -> 64.8 us; 32760 x 2048 x 2048 with the
+  // weights first: 127.7 -> 132.0 us).
+  constexpr int kRefillFirst = W_FIRST ? 2 : 1;
   static_assert(BM <= kWaves * 64 && BN <= kWaves * 64, "one epilogue operand per thread");
   static_assert(!FUSED || STAGES == 2, "the single-launch prologue's fill order assumes two stages");
   static_assert(!PERSIST || (!FUSED && STAGES == 2 && kWaves == 8),
@@ -643,12 +650,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_fp8_kernel(GemmArg
         else if (PERSIST) wait_vm_lgkm0<63>();
         else wait_vm_lgkm0<0>();
         block_barrier();
-        if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK, kSplitRefill ? 1 : 0);
+        if (t + STAGES < nst) issue(buf(s), (t + STAGES) * BK, kSplitRefill ? kRefillFirst : 0);
       }
       read_frags(buf((s + 1) % STAGES), 0, nxt);
     } else {
       // the second half of the refill issued at the previous stage barrier
-      if (kSplitRefill && t >= 1 && t + 1 < nst) issue(buf((s + 1) % STAGES), (t + 1) * BK, 2);
+      if (kSplitRefill && t >= 1 && t + 1 < nst) issue(buf((s + 1) % STAGES), (t + 1) * BK, 3 - kRefillFirst);
       read_frags(buf(s), h + 1, nxt);
     }
     mfma_all(cur);
@@ -837,7 +844,15 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
     wgs = std::min<int64_t>(tiles, cus >= kXcds ? (int64_t)(cus / kXcds) * kXcds : std::max(cus, 1));
     args.shares = (int)wgs;  // the persistent form's stride over the tiles
   }
-  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED, PERSIST>
+  const bool w_first = (int64_t)args.tiles_n * BN > (int64_t)args.tiles_m * BM;
+  if constexpr (S == 2 && WM * WN == 8) {  // the forms whose refills are split in halves
+    if (w_first) {
+      gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED, PERSIST, true>
+          <<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
+      return hipGetLastError();
+    }
+  }
+  gemm_fp8_kernel<BM, BN, WM, WN, S, BK, GM, FUSED, PERSIST, false>
       <<<dim3((unsigned)wgs), dim3(WM * WN * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
