@@ -148,3 +148,22 @@ def test_counters_two_kernels_on_one_grid_size(tmp_path):
     assert [r["launches"] for r in recs] == [2, 2]
     assert recs[0]["mfma_busy"] == pytest.approx(0.5) and recs[1]["mfma_busy"] == pytest.approx(0.7)
     assert recs[1]["algorithmic_flop"] == 2.0
+
+
+def test_bench_reports_traffic_only_for_the_current_gemm_sources(tmp_path):
+    # the bench's roofline.traffic comes from a committed counter record, and only while
+    # the GEMM sources are byte for byte the ones the counters were taken on
+    import hashlib
+    import bench
+
+    h = hashlib.sha256()
+    for p in bench.GEMM_SOURCES:
+        h.update(open(p, "rb").read())
+    rec = {"hbm_bytes_per_launch": 123456789.0, "gemm_source_sha256": h.hexdigest()}
+    good = tmp_path / "good.json"
+    good.write_text(json.dumps(rec))
+    assert bench.traffic_from_profile(str(good)) == 123456789.0
+    stale = tmp_path / "stale.json"
+    stale.write_text(json.dumps(dict(rec, gemm_source_sha256="0" * 64)))
+    assert bench.traffic_from_profile(str(stale)) is None
+    assert bench.traffic_from_profile(str(tmp_path / "missing.json")) is None
