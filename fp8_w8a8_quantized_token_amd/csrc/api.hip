@@ -517,9 +517,36 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
     config[i] = plan_bucket_config(plans[i], m);
     if (!grid_fits(config[i], m, plans[i]->n)) return FP8W8A8_ERR_BAD_SHAPE;
   }
-  bool grouped = nplans > 1 && (config[0] == kW8A8Persistent || config[0] == kW8A8Skinny);
-  for (int i = 1; i < nplans; ++i)
-    if (config[i] != config[0]) grouped = false;
+  // One launch for the group: when every plan takes the skinny form; or when every plan
+  // takes the 256 x 256 tiles (configuration 0, or its persistent form 6, which compute
+  // every tile alike) at a k where a single plan may take the persistent form, and one
+  // persistent launch needs fewer rounds of tiles over the CUs than the separate launches,
+  // or as many, all of them full. (Q, K and V at 8192 tokens: 256 tiles each, one round
+  // apiece, 768 together, three full rounds: 92.7 -> 84.9 us. At 6144 tokens, 192 tiles
+  // each: three rounds either way, the joint third a quarter full: 75.8 -> 79.5 us.)
+  bool grouped = false;
+  if (nplans > 1) {
+    bool skinny = true, big_tiles = p0->k >= 2048 && p0->k <= 4096;
+    for (int i = 0; i < nplans; ++i) {
+      skinny = skinny && config[i] == kW8A8Skinny;
+      big_tiles = big_tiles && (config[i] == 0 || config[i] == kW8A8Persistent);
+    }
+    if (skinny) {
+      grouped = true;
+    } else if (big_tiles) {
+      const int64_t c = std::max(8, p0->cu_count / 8 * 8);  // the persistent grid
+      int64_t tiles = 0, rounds_apart = 0;
+      for (int i = 0; i < nplans; ++i) {
+        const int64_t t = gemm_workgroups(0, m, plans[i]->n);
+        tiles += t;
+        rounds_apart += (t + c - 1) / c;
+      }
+      const int64_t rounds_joint = (tiles + c - 1) / c;
+      grouped = rounds_joint < rounds_apart || (rounds_joint == rounds_apart && tiles % c == 0);
+      if (grouped)
+        for (int i = 0; i < nplans; ++i) config[i] = kW8A8Persistent;
+    }
+  }
   if (grouped && config[0] == kW8A8Skinny) {  // the joint grid must fit as each plan's does
     int64_t wgs = 0;
     for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);

@@ -218,10 +218,12 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
  * nplans calls of fp8_linear_run(plans[i], m, a, a_kind, a_scale, outs_bf16[i], ...),
  * with the activation quantised once (FP8W8A8_A_BF16). The retrospective (section 3.4)
  * has the hidden states feed the Q, K and V projections (three weights, one input);
- * quantising them once per token serves all three. When every plan would run
- * the persistent GEMM configuration (6) at this m, the GEMMs go out as ONE launch
- * whose workgroups walk the tiles of all the problems (one first prologue and one
- * final output drain instead of nplans of each); when every plan would run the skinny
+ * quantising them once per token serves all three. When every plan would run the
+ * 256 x 256 tiles (configuration 0 or 6) at a k of 2048..4096 and one launch needs fewer
+ * rounds of tiles over the CUs than the separate ones (or as many, all full), the GEMMs go
+ * out as ONE persistent launch whose workgroups walk the tiles of all the problems (one
+ * first prologue and one final output drain instead of nplans of each); when every plan
+ * would run the skinny
  * configuration (5, a few tokens), as ONE launch over all the problems' channel blocks
  * (enough workgroups to fill the device, where one problem alone leaves it half idle);
  * otherwise each plan's GEMM runs as in fp8_linear_run. Outputs are bit-identical to the
