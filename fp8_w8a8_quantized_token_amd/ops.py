@@ -39,6 +39,13 @@ def _require(t, dtypes, name, dims=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on_device(device, **tensors):
+    """Every given tensor must live on the plan's device (the library launches there)."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the layer's weight on {device}")
+
+
 def _codes(t):
     """View e4m3fn codes as uint8 (float8_e4m3fn tensors and uint8 tensors are accepted)."""
     if t.dtype == torch.float8_e4m3fn:
@@ -244,6 +251,7 @@ class Fp8Linear:
             _require(out, (torch.bfloat16,), "out")
             if out.numel() != m * self.n:
                 raise ValueError("out has the wrong size")
+        _on_device(self.device, x=x2, x_scale=x_scale if fp8_in else None, out=out, workspace=ws)
         if m == 0:  # nothing to compute (an empty tensor has no device address to pass)
             return out.reshape(*lead, self.n)
         check(lib().fp8_linear_run(self._plan, m, _ptr(x2), kind, _ptr(x_scale) if fp8_in else None, _ptr(out),
@@ -300,6 +308,13 @@ def linear_group(linears, x, x_scale=None, outs=None, workspace=None):
             _require(o, (torch.bfloat16,), "out")
             if o.numel() != m * lin.n:
                 raise ValueError("an output has the wrong size")
+    dev = linears[0].device
+    for i, lin in enumerate(linears):
+        if lin.device != dev:
+            raise ValueError(f"layer {i} is on {lin.device}, layer 0 on {dev}")
+    _on_device(dev, x=x2, x_scale=x_scale if fp8_in else None, workspace=ws)
+    for i, o in enumerate(outs):
+        _on_device(dev, **{f"outs[{i}]": o})
     if m == 0:  # nothing to compute (an empty tensor has no device address to pass)
         return [o.reshape(*lead, lin.n) for o, lin in zip(outs, linears)]
     g = len(linears)
@@ -382,6 +397,9 @@ class Fp8WeightOnlyLinear:
             _require(out, (torch.bfloat16,), "out")
             if out.numel() != m * self.n:
                 raise ValueError("out has the wrong size")
+        _on_device(self.device, x=x2, out=out)
+        if m == 0:  # nothing to compute (an empty tensor has no device address to pass)
+            return out.reshape(*lead, self.n)
         check(lib().fp8_w8a16_run(self._plan, m, _ptr(x2), _ptr(out), _stream(x2)), "fp8_w8a16_run")
         return out.reshape(*lead, self.n)
 

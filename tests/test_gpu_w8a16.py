@@ -113,6 +113,8 @@ def test_selector_and_3d_input():
     assert out.shape == (4, 24, 400)
     ref, _, _ = _ref(case)
     assert_linear_close(out.reshape(96, 400), ref, "w8a16 3-d input")
+    empty = lin(torch.zeros((2, 0, 272), dtype=torch.bfloat16, device=dev))  # no tokens: an empty output
+    assert empty.shape == (2, 0, 400)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
