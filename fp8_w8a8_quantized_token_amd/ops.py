@@ -60,6 +60,8 @@ def quant_rows(x):
     m, k = x2.shape
     q = torch.empty((m, k), dtype=torch.uint8, device=x2.device)
     s = torch.empty((m,), dtype=torch.float32, device=x2.device)
+    if m == 0:  # no tokens (an empty tensor has no device address to pass)
+        return q, s
     check(lib().fp8_quant_rows(_ptr(x2), m, k, _ptr(q), _ptr(s), _stream(x2)), "fp8_quant_rows")
     return q, s
 
@@ -106,6 +108,8 @@ def act_rows(x, table, out=None):
     _require(y, (torch.bfloat16,), "out")
     if y.numel() != m * k:
         raise ValueError("out must hold as many elements as x")
+    if m == 0:
+        return y.view(x.shape)
     check(lib().fp8_act_rows(_ptr(x2), m, k, _ptr(table), _ptr(y), _stream(x2)), "fp8_act_rows")
     return y.view(x.shape)
 
@@ -122,6 +126,8 @@ def act_quant_rows(x, table, q=None, scale=None):
     _require(s, (torch.float32,), "scale")
     if q.numel() != m * k or s.numel() != m:
         raise ValueError("q must hold m * k codes and scale m values")
+    if m == 0:
+        return q, s
     check(lib().fp8_act_quant_rows(_ptr(x2), m, k, _ptr(table), _ptr(q), _ptr(s), _stream(x2)),
           "fp8_act_quant_rows")
     return q, s
@@ -144,6 +150,8 @@ def quant_tensor(x, fmt="e4m3fn", workspace=None, form="auto"):
         raise ValueError(f"unknown form {form!r}; expected one of {sorted(_lib.TENSOR_FORMS)}")
     xc = x.contiguous()
     _require(xc, (torch.bfloat16,), "x")
+    if xc.numel() == 0:  # the converter treats an empty tensor as invalid input
+        raise ValueError("empty tensor: there is nothing to quantise and no scale to derive")
     q = torch.empty(xc.shape, dtype=torch.uint8, device=xc.device)
     s = torch.empty((1,), dtype=torch.float32, device=xc.device)
     ws_bytes = lib().fp8_quant_tensor_workspace_bytes()
@@ -165,6 +173,8 @@ def dequant_tensor(q, scale, fmt="e4m3fn"):
     _require(qc, (torch.uint8,), "q")
     _require(scale, (torch.float32,), "scale")
     out = torch.empty(qc.shape, dtype=torch.float32, device=qc.device)
+    if qc.numel() == 0:
+        return out
     check(lib().fp8_dequant_tensor(_ptr(qc), qc.numel(), FORMATS[fmt], _ptr(scale), _ptr(out), _stream(qc)),
           "fp8_dequant_tensor")
     return out

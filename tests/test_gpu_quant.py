@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp8_w8a8_quantized_token_amd as fp8
 from fp8_w8a8_quantized_token_amd import quant_rows, quant_weights_per_channel
 from oracle import cref, quant as oq
 from tests._helpers import assert_codes_equal, require_gpu
@@ -170,3 +171,20 @@ def test_exhaustive_bf16_pairs():
         diff = q.cpu().numpy() != eq
         mismatches += int(diff.sum())
         assert mismatches == 0, f"{mismatches} codes differ (amax chunk starting at bf16 {start + 1:#06x})"
+
+
+def test_empty_inputs_through_the_bindings():
+    # no tokens: empty outputs of the right shapes and nothing launched; the per-tensor
+    # converter treats an empty tensor as invalid input
+    dev = require_gpu()
+    x = torch.zeros((0, 2048), dtype=torch.bfloat16, device=dev)
+    q, s = fp8.quant_rows(x)
+    assert q.shape == (0, 2048) and s.shape == (0,)
+    table = fp8.act_table("gelu_tanh", dev)
+    assert fp8.act_rows(x, table).shape == (0, 2048)
+    q, s = fp8.act_quant_rows(x, table)
+    assert q.shape == (0, 2048) and s.shape == (0,)
+    with pytest.raises(ValueError, match="empty"):
+        fp8.quant_tensor(x)
+    d = fp8.dequant_tensor(torch.zeros((0, 16), dtype=torch.uint8, device=dev), torch.ones((1,), device=dev))
+    assert d.shape == (0, 16)
