@@ -132,7 +132,10 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
   const float r = 1.0f / s;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride) {
+  // back to front: the maxima pass read the tensor front to back, so its last part is the
+  // likeliest to still sit in the memory-side cache
+  for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < n16; j += stride) {
+    const int64_t i = n16 - 1 - j;
     const uint4 a = x[2 * i], b = x[2 * i + 1];
     const uint4 o = quant16_fmt<FMT>(a, b, amax, s, r);
     // non-temporal: the codes are not read again here (8192 x 2048: 19.1 -> 18.2 us)
