@@ -431,8 +431,8 @@ def block_bench(torch, fp8, lib, dev, stream, steps, config):
 
 def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
     """Per-tensor quantisation (both formats), HBM-resident rotating inputs: the form
-    fp8_quant_tensor picks (one pass for e4m3fn up to 65536 elements per CU, else two
-    passes), and at the shape that fits one pass the other form beside it."""
+    fp8_quant_tensor picks (one pass up to 65536 elements per CU, else two passes), and
+    at the shape that fits one pass the other form beside it."""
     from fp8_w8a8_quantized_token_amd import _lib
     from workloads.synth import activation
     sptr = ctypes.c_void_p(stream.cuda_stream)

@@ -23,11 +23,14 @@
 //   * Two passes, for larger tensors: amax_partials writes one maximum per workgroup
 //     into the caller's workspace; quant_tensor reduces those partials in every
 //     workgroup (at most 1024 values, one LDS pass), derives s, writes it once, and
-//     quantises its grid-stride share, reading the input again. e4m3fn
-// quotients reuse the per-token quantiser's arithmetic (quant_row.h, including its
-// divide-free fast path); e5m2 quotients take an IEEE division, since its subnormal
-// range reaches quotients below the fast path's proven range. v_cvt_pk_bf8_f32 /
-// v_cvt_pk_fp8_f32 round to nearest even into the OCP encodings and do not saturate.
+//     quantises its grid-stride share, reading the input again. Both formats form
+// their quotients with the per-token quantiser's arithmetic (quant_row.h): divide-free
+// from amax >= 2^-80, an IEEE division below. For the e5m2 scale fl32(amax / 57344), over
+// every pair of finite bf16 values (x, amax >= 2^-80) with |x| <= amax, the divide-free
+// quotient differs from fl32(x / s) only where both lie below 2^-17.03 in magnitude with
+// the same sign, and every such value encodes to the same signed zero (e5m2's smallest
+// subnormal is 2^-16). v_cvt_pk_bf8_f32 / v_cvt_pk_fp8_f32 round to nearest even into the
+// OCP encodings and do not saturate.
 // e4m3fn quotients stay below 464 (the midpoint above 448) for every bf16 pair
 // (x, amax), fp32-subnormal scales included. e5m2 quotients do not: for a bf16 amax of
 // 1..3 x 2^-133 the scale fl32(amax / 57344) is an fp32 subnormal of 1..3 units that
@@ -55,16 +58,18 @@ __device__ __forceinline__ uint32_t pack4_bf8(float a, float b, float c, float d
 // Clamp a quotient to the largest finite e5m2 magnitude (57344), sign kept.
 __device__ __forceinline__ float sat_e5m2(float q) { return fminf(fmaxf(q, -57344.0f), 57344.0f); }
 
-// 16 bf16 (two uint4) -> 16 e5m2 codes: IEEE quotient (or the value itself when s == 0)
-__device__ __forceinline__ uint4 quant16_e5m2(const uint4& a, const uint4& b, float s, bool zero) {
+// 16 bf16 (two uint4) -> 16 e5m2 codes, quotients formed as quant_row.h's mode M forms them
+template <qrow::Mode M>
+__device__ __forceinline__ uint4 quant16_e5m2(const uint4& a, const uint4& b, float s, float r) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t u0 = w[2 * i], u1 = w[2 * i + 1];
-    const float x0 = qrow::bf16_lo(u0), x1 = qrow::bf16_hi(u0), x2 = qrow::bf16_lo(u1), x3 = qrow::bf16_hi(u1);
-    o[i] = zero ? pack4_bf8(x0, x1, x2, x3) : pack4_bf8(sat_e5m2(x0 / s), sat_e5m2(x1 / s), sat_e5m2(x2 / s),
-                                                         sat_e5m2(x3 / s));
+    o[i] = pack4_bf8(sat_e5m2(qrow::quotient<M>(qrow::bf16_lo(u0), s, r)),
+                     sat_e5m2(qrow::quotient<M>(qrow::bf16_hi(u0), s, r)),
+                     sat_e5m2(qrow::quotient<M>(qrow::bf16_lo(u1), s, r)),
+                     sat_e5m2(qrow::quotient<M>(qrow::bf16_hi(u1), s, r)));
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -93,7 +98,9 @@ __device__ __forceinline__ float abs_max16(const uint4& a, const uint4& b, float
 template <int FMT>
 __device__ __forceinline__ uint4 quant16_fmt(const uint4& a, const uint4& b, float amax, float s, float r) {
   if constexpr (FMT == FP8W8A8_FMT_E5M2) {
-    return quant16_e5m2(a, b, s, amax == 0.0f);
+    if (amax >= qrow::kTinyAmax) return quant16_e5m2<qrow::Mode::kFast>(a, b, s, r);
+    if (amax == 0.0f) return quant16_e5m2<qrow::Mode::kZero>(a, b, s, r);
+    return quant16_e5m2<qrow::Mode::kExact>(a, b, s, r);
   } else {
     if (amax >= qrow::kTinyAmax) return qrow::quant16<qrow::Mode::kFast>(a, b, s, r);
     if (amax == 0.0f) return qrow::quant16<qrow::Mode::kZero>(a, b, s, r);
@@ -328,9 +335,7 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t numel, int fmt, uint8_
   while (np <= kOnePassMaxNP && groups_max * kOnePassBlock * np < n16) np *= 2;
   if (form == kTensorOnePass || form == kTensorOnePassNoWait) {
     if (np > kOnePassMaxNP) return hipErrorInvalidValue;
-  } else if (form == kTensorTwoPass || fmt == FP8W8A8_FMT_E5M2) {
-    // e5m2's IEEE divisions all run after the wait in one pass, where nothing overlaps
-    // them: 19.2 us against 18.8 in two passes at 8192 x 2048 (e4m3fn: 14.9 against 18.0)
+  } else if (form == kTensorTwoPass) {
     np = kOnePassMaxNP + 1;
   }
   if (np <= kOnePassMaxNP) {

@@ -366,9 +366,9 @@ int fp8_quant_gemm(int64_t m, int64_t n, int64_t k, const void* a_bf16, const vo
  *   workspace  device, fp8_quant_tensor_workspace_bytes() bytes, 16-byte aligned, scratch
  *              (per-workgroup maxima); its contents need no initialisation; two
  *              calls that overlap in time must not share it
- * Two launches on `stream`. Inputs must be finite. An e4m3fn tensor that fits in the
- * registers of one workgroup per compute unit (numel <= 65536 x CUs: 16.8 M elements,
- * 32 MiB of bf16, on 256 CUs) is read once: a small launch marks the maxima unwritten,
+ * Two launches on `stream`. Inputs must be finite. A tensor that fits in the registers
+ * of one workgroup per compute unit (numel <= 65536 x CUs: 16.8 M elements, 32 MiB of
+ * bf16, on 256 CUs) is read once: a small launch marks the maxima unwritten,
  * then the workgroups hold their shares, publish their maxima, wait for the largest
  * and quantise what they hold. Other tensors are read twice (maxima, then codes).
  */

@@ -8,7 +8,9 @@ that fits; two passes: just above it), every form on the same tensors (the one-p
 also with no workgroup waiting for the others), the maximum held by the first or the last
 workgroup only; both forms captured in a HIP graph and replayed with new inputs; every finite bf16 value through each format's
 conversion (a tensor whose amax equals the format's largest value has scale 1, so
-the quotients are the values themselves); zero tensors; tensors whose scale is an
+the quotients are the values themselves); quotients near each format's rounding floor
+for every exponent of amax (where the divide-free quotient may be an ulp off); zero
+tensors; tensors whose scale is an
 fp32 subnormal (the exact-division path), down to the smallest bf16 amax values, whose
 e5m2 quotients overflow the format and must saturate; the dequantisation of every code.
 """
@@ -19,6 +21,7 @@ import torch
 
 import fp8_w8a8_quantized_token_amd as fp8
 from oracle import e4m3, e5m2, tensor_quant as otq
+from oracle.quant import bf16_bits_to_f32
 from tests._helpers import require_gpu
 from workloads import bf16_bits, make_case
 
@@ -137,6 +140,31 @@ def test_smallest_subnormal_amax(fmt, amax_bits):
     body[5] = amax_bits
     body[17] = amax_bits | 0x8000
     _check(body, fmt, dev)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quotients_near_the_rounding_floor_at_every_scale_exponent(fmt):
+    # The kernels form x / s without a divide from amax >= 2^-80 (a reciprocal and one fma
+    # correction), which can differ from fl32(x / s) by an ulp where the quotient is tiny.
+    # For every bf16 exponent of amax (two mantissas each), every bf16 x whose quotient
+    # lies within a few binades of the format's rounding floor (half its smallest
+    # subnormal: 2^-10 for e4m3fn, 2^-17 for e5m2), both signs; codes bit for bit.
+    dev = require_gpu()
+    floor = -10 if fmt == "e4m3fn" else -17
+    fmax = 448.0 if fmt == "e4m3fn" else 57344.0
+    mant = np.arange(128, dtype=np.uint16)
+    for e in range(1, 255):
+        for m in (0x00, 0x5B):
+            amax_bits = np.uint16((e << 7) | m)
+            amax = float(bf16_bits_to_f32(np.array([amax_bits], np.uint16))[0])
+            es = int(np.floor(np.log2(np.float32(amax / fmax))))  # exponent of the scale
+            fields = [f for f in range(es + floor - 3 + 127, es + floor + 4 + 127) if 0 <= f <= 254]
+            if not fields:
+                continue
+            mags = np.concatenate([(np.uint16(f) << 7) | mant for f in fields])
+            bits = np.concatenate([mags, mags | np.uint16(0x8000), [amax_bits, amax_bits | np.uint16(0x8000)]])
+            bits = np.concatenate([bits, np.zeros((-len(bits)) % 16, np.uint16)]).astype(np.uint16)
+            _check(bits, fmt, dev)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
