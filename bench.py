@@ -445,7 +445,7 @@ def tensor_quant_bench(torch, fp8, lib, dev, stream, steps):
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         fits = rows * cols <= 65536 * cus
         for fmt_name, fmt in (("e4m3fn", _lib.FMT_E4M3FN), ("e5m2", _lib.FMT_E5M2)):
-            one_pass = fits and fmt == _lib.FMT_E4M3FN  # what fp8_quant_tensor picks
+            one_pass = fits  # what fp8_quant_tensor picks
             def timed(form):
                 def run(i):
                     st = lib.fp8_quant_tensor_form(form, ctypes.c_void_p(xs[i % nsets].data_ptr()), rows * cols, fmt,
