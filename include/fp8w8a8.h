@@ -24,7 +24,9 @@
  *   Scales are fp32: s [m], sW [n]. bias is bf16 [n] or NULL.
  *
  * Ownership. The caller allocates and frees every device buffer. The library
- * never allocates device memory. A plan is a small host object owned by the
+ * never allocates device memory at run time; the only device memory it holds is
+ * the fixed scratch array of fp8_linear_run_noalloc, part of its code object on each
+ * GPU it runs on. A plan is a small host object owned by the
  * library (create / destroy); it borrows the weight, weight-scale and bias
  * pointers, which must stay valid while the plan is used.
  *
