@@ -166,6 +166,31 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
     if (!filler) return;
     const int ke0 = s * KE;  // first k element of the stage
     const bool va0 = ke0 + 8 * fac0 < K, va1 = ke0 + 8 * fac1 < K;
+    if constexpr (kFillWaves < kWaves) {
+      // As in the FP8 GEMM: one lane base per operand and call (every activation fill of
+      // a wave has its first row's parity), each fill adding its uniform row offset; a
+      // lane past k starts from kOutOfRange and stays past the descriptor's end.
+      static_assert((kFillWaves * kARpf) % 16 == 0, "one row parity per filling wave");
+      static_assert((int64_t)(BM > BN ? BM : BN) * 2 * FP8W8A8_MAX_DIM <= (int64_t)1 << 29 &&
+                        kOutOfRange == 0x80000000u,
+                    "out-of-range offsets stay out of range");
+      const bool odd = ((wave * kARpf) & 15) != 0;
+      const uint32_t ba = (odd ? va1 : va0) ? (odd ? faoff1 : faoff0) + (uint32_t)ke0 * 2u : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < FA; ++j) {
+        const int g = wave + j * kFillWaves;
+        dma16(rsrc_a, (uint32_t)reinterpret_cast<uintptr_t>(base + g * 1024),
+              ba + (uint32_t)(g * kARpf) * (uint32_t)K * 2u);
+      }
+      const uint32_t bw = ke0 + 16 * fwc < K ? fwoff + (uint32_t)ke0 : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < FW; ++j) {
+        const int g = wave + j * kFillWaves;
+        dma16(rsrc_w, (uint32_t)reinterpret_cast<uintptr_t>(base + kABytes + g * 1024),
+              bw + (uint32_t)(g * kWRpf) * (uint32_t)K);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < FA; ++j) {
       const int g = wave + j * kFillWaves;
@@ -298,7 +323,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_w8a16_kernel(W16Ar
   };
   constexpr int kUnroll = STAGES * H;  // whole stage ring; H is even, so is the unroll
   static_assert(kUnroll % 2 == 0, "cur / nxt alternate within the unrolled ring");
-  for (int u0 = 0; u0 < nsub; u0 += kUnroll) {
+  // whole rings without a bound check per sub-step, then the rest with one
+  int u0 = 0;
+  for (; u0 + kUnroll <= nsub; u0 += kUnroll) {
+#pragma unroll
+    for (int v = 0; v < kUnroll; v += 2) {
+      sub(u0 + v, (v / H) % STAGES, v % H, f0, f1);
+      sub(u0 + v + 1, ((v + 1) / H) % STAGES, (v + 1) % H, f1, f0);
+    }
+  }
+  for (; u0 < nsub; u0 += kUnroll) {
 #pragma unroll
     for (int v = 0; v < kUnroll; v += 2) {
       if (u0 + v < nsub) sub(u0 + v, (v / H) % STAGES, v % H, f0, f1);
