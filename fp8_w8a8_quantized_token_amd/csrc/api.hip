@@ -159,6 +159,7 @@ struct Family {
   TileModel (*model)(int);
   int skinny;           // configuration for m <= skinny_max_m (outside the tile model), or -1
   int64_t skinny_max_m;
+  int skinny_wide;      // its form with more channels per workgroup, for grids wider than the CUs, or -1
   int persistent;       // persistent form of configuration 0 (outside the tile model), or -1
 };
 // m buckets: rows <= bound[b] use the configuration chosen at that bound; the last bucket
@@ -177,6 +178,15 @@ static_assert(sizeof(kW8A16Bounds) / sizeof(int64_t) <= kMaxBuckets, "bucket cou
 // 4.0 against 9.0. Above 32 tokens it loads the weight once per 32 tokens and loses at
 // wide n (m = 64, n = 8192: 14.8 against 9.6 us), so it serves m <= 32 only.
 constexpr int kW8A8Skinny = 5;
+// Configuration 7 is the same weight stream with 32 channels per workgroup: the activation
+// is loaded once for twice the weight bytes, on half the workgroups; every output is
+// bit-identical to configuration 5's. Timed against it (graph-replayed launches over
+// > 256 MB of rotating weights, random codes, m = 26, k = 2048): 384 workgroups of
+// configuration 5 (n = 6144, the grid of the Q/K/V encoder group) 8.00 -> 6.95 us, 512
+// (n = 8192) 8.29 -> 7.31; at 256 or fewer it loses (n = 4096: 5.87 against 7.21 us, n =
+// 2048: 5.16 against 6.57, k = 8192: 12.7 against 17.1). So it serves the skinny products
+// whose configuration-5 grid exceeds the CU count.
+constexpr int kW8A8SkinnyWide = 7;
 // The persistent form of the 256 x 256 tiles (one workgroup per CU walking its tiles, the
 // next tile's first stages requested before the current tile's epilogue) is output-for-
 // output identical to configuration 0. Timed against it on 32 shapes (m 2048 .. 32760,
@@ -187,9 +197,10 @@ constexpr int kW8A8Skinny = 5;
 // saved prologue does not pay for them, and at k = 1024 the results went either way.
 constexpr int kW8A8Persistent = 6;
 const Family kW8A8{kW8A8Bounds, (int)(sizeof(kW8A8Bounds) / sizeof(int64_t)), gemm_config_count, gemm_config,
-                   gemm_workgroups, gemm_threads, w8a8_tile_model, kW8A8Skinny, 32, kW8A8Persistent};
+                   gemm_workgroups, gemm_threads, w8a8_tile_model, kW8A8Skinny, 32, kW8A8SkinnyWide,
+                   kW8A8Persistent};
 const Family kW8A16{kW8A16Bounds, (int)(sizeof(kW8A16Bounds) / sizeof(int64_t)), w8a16_config_count, w8a16_config,
-                    w8a16_workgroups, w8a16_threads, w8a16_tile_model, -1, 0, -1};
+                    w8a16_workgroups, w8a16_threads, w8a16_tile_model, -1, 0, -1, -1};
 
 bool grid_fits(const Family& f, int config, int64_t m, int64_t n) {
   return f.workgroups(config, m, n) * f.threads(config) < kMaxGridThreads;
@@ -210,11 +221,18 @@ double model_time(const Family& f, int c, int64_t m, int64_t n, int64_t k, int c
 }
 
 int choose_config(const Family& f, int64_t m, int64_t n, int64_t k, int cus) {
-  if (f.skinny >= 0 && m <= f.skinny_max_m && grid_fits(f, f.skinny, m, n)) return f.skinny;
+  if (f.skinny >= 0 && m <= f.skinny_max_m) {
+    if (f.skinny_wide >= 0 && f.workgroups(f.skinny, m, n) > cus && grid_fits(f, f.skinny_wide, m, n))
+      return f.skinny_wide;
+    if (grid_fits(f, f.skinny, m, n)) return f.skinny;
+  }
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < f.count(); ++c) {
-    if (c == f.skinny || c == f.persistent || !grid_fits(f, c, m, n)) continue;
+    // the weight-stream forms (no LDS pipeline) are outside the tile model
+    if (c == f.skinny || c == f.skinny_wide || c == f.persistent || f.config(c)->stages == 0 ||
+        !grid_fits(f, c, m, n))
+      continue;
     const double t = model_time(f, c, m, n, k, cus);
     if (best < 0 || t < best_t) {
       best = c;
@@ -517,7 +535,8 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
     config[i] = plan_bucket_config(plans[i], m);
     if (!grid_fits(config[i], m, plans[i]->n)) return FP8W8A8_ERR_BAD_SHAPE;
   }
-  // One launch for the group: when every plan takes the skinny form; or when every plan
+  // One launch for the group: when every plan takes a skinny form (in the wide one, 7, when
+  // the problems' 16-channel blocks together outnumber the CUs); or when every plan
   // takes the 256 x 256 tiles (configuration 0, or its persistent form 6, which compute
   // every tile alike) at a k where a single plan may take the persistent form, and one
   // persistent launch needs fewer rounds of tiles over the CUs than the separate launches,
@@ -525,14 +544,23 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
   // apiece, 768 together, three full rounds: 92.7 -> 84.9 us. At 6144 tokens, 192 tiles
   // each: three rounds either way, the joint third a quarter full: 75.8 -> 79.5 us.)
   bool grouped = false;
+  int group_form = -1;  // the configuration of the one launch
   if (nplans > 1) {
     bool skinny = true, big_tiles = p0->k >= 2048 && p0->k <= 4096;
     for (int i = 0; i < nplans; ++i) {
-      skinny = skinny && config[i] == kW8A8Skinny;
+      skinny = skinny && (config[i] == kW8A8Skinny || config[i] == kW8A8SkinnyWide);
       big_tiles = big_tiles && (config[i] == 0 || config[i] == kW8A8Persistent);
     }
     if (skinny) {
-      grouped = true;
+      // the joint grid takes the wide form when the 16-channel blocks of all the
+      // problems together exceed the CU count (the rule of a single plan, above)
+      int64_t blocks = 0;
+      for (int i = 0; i < nplans; ++i) blocks += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);
+      group_form = blocks > p0->cu_count ? kW8A8SkinnyWide : kW8A8Skinny;
+      // and the joint grid must fit as each plan's does
+      int64_t wgs = 0;
+      for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(group_form, m, plans[i]->n);
+      grouped = wgs * gemm_threads(group_form) < kMaxGridThreads;
     } else if (big_tiles) {
       const int64_t c = std::max(8, p0->cu_count / 8 * 8);  // the persistent grid
       int64_t tiles = 0, rounds_apart = 0;
@@ -543,14 +571,8 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
       }
       const int64_t rounds_joint = (tiles + c - 1) / c;
       grouped = rounds_joint < rounds_apart || (rounds_joint == rounds_apart && tiles % c == 0);
-      if (grouped)
-        for (int i = 0; i < nplans; ++i) config[i] = kW8A8Persistent;
+      group_form = kW8A8Persistent;
     }
-  }
-  if (grouped && config[0] == kW8A8Skinny) {  // the joint grid must fit as each plan's does
-    int64_t wgs = 0;
-    for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);
-    if (wgs * gemm_threads(kW8A8Skinny) >= kMaxGridThreads) grouped = false;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* qa = static_cast<const uint8_t*>(a);
@@ -568,7 +590,7 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
     for (int i = 0; i < nplans; ++i)
       probs[i] = GroupProblem{plans[i]->w, plans[i]->w_scale, plans[i]->bias, static_cast<uint16_t*>(outs_bf16[i]),
                               plans[i]->n};
-    return launch_gemm_group(config[0], m, p0->k, qa, sa, nplans, probs, p0->cu_count, s) == hipSuccess
+    return launch_gemm_group(group_form, m, p0->k, qa, sa, nplans, probs, p0->cu_count, s) == hipSuccess
                ? FP8W8A8_OK
                : FP8W8A8_ERR_HIP;
   }

@@ -900,9 +900,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
 // how many CUs pull weight bytes at once and how much else each of them must load. The
 // tiled kernel's smallest tile (64 x 64) gives one workgroup per 64 channels (32 for
 // n = 2048) that walks k through a three-stage LDS pipeline, so most CUs idle and each
-// active one waits on a chain of dependent stages. Here a workgroup owns NW = 16 channels
-// and 16 * MT tokens (grid: ceil(n / 16) x ceil(m / (16 MT)) workgroups, 128 for the
-// encoder GEMM), and its WAVES waves split k between them: wave w takes the 128-byte
+// active one waits on a chain of dependent stages. Here a workgroup owns NW = 16 NF channels
+// and 16 * MT tokens (grid: ceil(n / NW) x ceil(m / (16 MT)) workgroups; with NF = 1, 128
+// for the encoder GEMM, and NF = 2 halves the grid where it would exceed the CUs, so that
+// the activation, which every workgroup loads in full, is loaded once per 32 channels
+// rather than 16), and its WAVES waves split k between them: wave w takes the 128-byte
 // k-steps w, w + WAVES, ... . Each wave loads its operand fragments straight from
 // memory into registers (no LDS staging, no barrier in the loop), two k-steps per batch
 // with the next batch requested before the current one is multiplied, and runs
@@ -919,60 +921,96 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream, int cus = 0) {
 // 4 (l / 16) + i (channels), i = 0..3.
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kSkinnyNW = 16;     // channels per workgroup
 constexpr int kSkinnyWaves = 8;   // waves per workgroup, splitting k
 constexpr int kSkinnyBatch = 2;   // 128-byte k-steps per load batch
 
-template <int MT>
+template <int MT, int NF>
 struct SkinnyFrags {
-  v8i w[kSkinnyBatch];
+  v8i w[kSkinnyBatch][NF];
   v8i a[kSkinnyBatch][MT];
 };
 
-// GROUPED: the problems of GemmArgs' group side by side along the workgroups' column
-// blocks (g_tn_end counts 16-channel blocks here); each workgroup looks its problem up.
-template <int MT, bool GROUPED = false>
+// NF: 16-channel weight fragments per wave (the workgroup owns 16 NF channels). Each
+// fragment's sum runs exactly as with NF = 1 (same k-steps per wave, same order, same
+// fixed-order sum over the waves), so every output is bit-identical whatever NF is; a
+// larger NF loads the activation once for more weight bytes.
+// GROUPED: column block blockIdx.x of problem blockIdx.y of GemmArgs' group, token block
+// blockIdx.z (a 3-D grid, as many column blocks as the widest problem has; a workgroup
+// past its problem's width exits at once). The problem's fields are read straight from
+// the kernel arguments at that index, with no search over the group, and all the
+// arguments are in registers before the width test, so they cost one round trip, as a
+// single problem's do.
+template <int MT, int NF, bool GROUPED = false>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs args) {
   constexpr int WAVES = kSkinnyWaves;
+  constexpr int NW = 16 * NF;  // channels per workgroup
   constexpr int TM = 16 * MT;  // tokens per workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tn = blockIdx.x % args.tiles_n, tm = blockIdx.x / args.tiles_n;
-  const TileProblem pr = tile_problem<kSkinnyNW, GROUPED>(kernarg_args(), tn);
+  int tn, tm;
+  TileProblem pr;
+  const uint8_t* qa = args.qa;
+  const float* a_scale = args.a_scale;
+  int K = args.k, M = args.m;
+  if constexpr (GROUPED) {
+    tn = blockIdx.x;
+    tm = blockIdx.z;
+    const int p = blockIdx.y;
+    const KernargGemmArgs k = kernarg_args();
+    pr = TileProblem{k->g_qw[p], k->g_ws[p], k->g_bias[p], k->g_out[p], k->g_n[p], tn * NW};
+    // every argument in registers here (one wait for all of them), not loaded after the test
+    asm volatile("" ::"s"(pr.qw), "s"(pr.ws), "s"(pr.bias), "s"(pr.out), "s"(pr.n), "s"(qa), "s"(a_scale),
+                 "s"(K), "s"(M));
+    if (pr.n0 >= pr.n) return;  // the whole workgroup, before any barrier
+  } else {
+    tn = blockIdx.x % args.tiles_n;
+    tm = blockIdx.x / args.tiles_n;
+    pr = tile_problem<NW, false>(kernarg_args(), tn);
+  }
   const int n = pr.n, n0 = pr.n0, m0 = tm * TM;
-  const int K = args.k;
-  const int rows_a = min(TM, args.m - m0);
-  const int rows_w = min(kSkinnyNW, n - n0);
+  const int rows_a = min(TM, M - m0);
+  const int rows_w = min(NW, n - n0);
   const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.qa) + (int64_t)m0 * K, 0,
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qa) + (int64_t)m0 * K, 0,
                                         (uint32_t)rows_a * (uint32_t)K, kBufferConfig);
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pr.qw) + (int64_t)n0 * K, 0,
                                         (uint32_t)rows_w * (uint32_t)K, kBufferConfig);
 
-  // epilogue operands of this thread's output (token t / 16, channel t % 16: every output of
-  // the workgroup's tile has one thread, since TM * NW == WAVES * 64), requested now
-  static_assert(TM * kSkinnyNW == WAVES * 64, "one output per thread");
-  const int et = threadIdx.x / kSkinnyNW, ec = threadIdx.x % kSkinnyNW;
-  const bool evalid = et < rows_a && ec < rows_w;
-  float e_sa = 0.0f, e_sw = 0.0f, e_b = 0.0f;
-  if (evalid) {
-    e_sa = args.a_scale[m0 + et];
-    e_sw = pr.ws[n0 + ec];
-    if (pr.bias) e_b = __uint_as_float((uint32_t)pr.bias[n0 + ec] << 16);
+  // epilogue operands of this thread's NF outputs (output o = threadIdx.x + j WAVES 64 is
+  // token o / NW, channel o % NW: every output of the workgroup's tile has one thread, since
+  // TM * NW == NF * WAVES * 64), requested now and used only after the k loop. The loads
+  // take no branch (indices clamped into the tile; outputs outside it are never stored, and
+  // without a bias the weight scales stand in as an in-bounds source) and the bias stays
+  // raw until the epilogue, so no wave waits for them before its operand loads go out.
+  static_assert(TM * NW == NF * WAVES * 64, "NF outputs per thread");
+  const uint16_t* bias_src = pr.bias ? pr.bias : reinterpret_cast<const uint16_t*>(pr.ws);
+  float e_sa[NF], e_sw[NF];
+  uint32_t e_b[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int o = threadIdx.x + j * WAVES * 64;
+    const int ct = min(o / NW, rows_a - 1), cc = min(o % NW, rows_w - 1);
+    e_sa[j] = a_scale[m0 + ct];
+    e_sw[j] = pr.ws[n0 + cc];
+    e_b[j] = bias_src[n0 + cc];
   }
 
   const int r = lane & 15, q = lane >> 4;
   const uint32_t row_off = (uint32_t)r * (uint32_t)K;
   const int steps = (K + 127) / 128;
-  auto load = [&](int step, v8i& w, v8i* a) {
+  auto load = [&](int step, v8i* w, v8i* a) {
     // chunk c of the step's 128 bytes holds k bytes [16 c, 16 c + 16); lanes past k read zeros
     const int k0 = step * 128 + 16 * q, k1 = k0 + 64;
     const uint32_t o0 = k0 < K ? row_off + (uint32_t)k0 : kOutOfRange;
     const uint32_t o1 = k1 < K ? row_off + (uint32_t)k1 : kOutOfRange;
-    const v4u w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o0, 0, 0);
-    const v4u w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o1, 0, 0);
-    w = v8i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint32_t d = (uint32_t)(16 * f) * (uint32_t)K;
+      const v4u w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, o0 == kOutOfRange ? o0 : o0 + d, 0, 0);
+      const v4u w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, o1 == kOutOfRange ? o1 : o1 + d, 0, 0);
+      w[f] = v8i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint32_t d = (uint32_t)(16 * t) * (uint32_t)K;
@@ -981,28 +1019,33 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
       a[t] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     }
   };
-  auto load_batch = [&](int first, SkinnyFrags<MT>& f) {
+  auto load_batch = [&](int first, SkinnyFrags<MT, NF>& fr) {
 #pragma unroll
     for (int b = 0; b < kSkinnyBatch; ++b) {
       const int step = first + b * WAVES;
-      if (step < steps) load(step, f.w[b], f.a[b]);
+      if (step < steps) load(step, fr.w[b], fr.a[b]);
     }
   };
 
-  v4f acc[MT];
+  v4f acc[NF][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  auto mfma_batch = [&](int first, const SkinnyFrags<MT>& f) {
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[f][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto mfma_batch = [&](int first, const SkinnyFrags<MT, NF>& fr) {
 #pragma unroll
     for (int b = 0; b < kSkinnyBatch; ++b)
       if (first + b * WAVES < steps)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.w[b], f.a[b][t], acc[t], 0, 0, 0, 0, 0, 0);
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[f][t] =
+                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fr.w[b][f], fr.a[b][t], acc[f][t], 0, 0, 0, 0, 0, 0);
   };
 
   constexpr int kStride = kSkinnyBatch * WAVES;  // k-steps between a wave's batches
-  SkinnyFrags<MT> f0, f1;
+  SkinnyFrags<MT, NF> f0, f1;
   load_batch(wave, f0);
   for (int s = wave; s < steps; s += 2 * kStride) {
     load_batch(s + kStride, f1);
@@ -1013,29 +1056,41 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_fp8_skinny(GemmArgs ar
   }
 
   // partial sums of every wave -> LDS, then a fixed-order sum per output
-  __shared__ v4f red[WAVES][MT][64];
+  __shared__ v4f red[WAVES][NF][MT][64];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][f][t][lane] = acc[f][t];
   __syncthreads();
-  // token et is column et % 16 of m-tile et / 16; channel ec is row ec of the result
-  const int src_lane = (et & 15) + 16 * (ec >> 2);
-  float sum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) sum += red[w][et >> 4][src_lane][ec & 3];
-  if (evalid) {
-    const float v = __builtin_fmaf(sum * e_sa, e_sw, e_b);
-    pr.out[(int64_t)(m0 + et) * n + n0 + ec] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+  for (int j = 0; j < NF; ++j) {
+    const int o = threadIdx.x + j * WAVES * 64, et = o / NW, ec = o % NW;
+    // token et is column et % 16 of m-tile et / 16; channel ec is row ec % 16 of fragment ec / 16
+    const int cf = ec >> 4, cr = ec & 15;
+    const int src_lane = (et & 15) + 16 * (cr >> 2);
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][cf][et >> 4][src_lane][cr & 3];
+    if (et < rows_a && ec < rows_w) {
+      const float b = pr.bias ? __uint_as_float(e_b[j] << 16) : 0.0f;
+      const float v = __builtin_fmaf(sum * e_sa[j], e_sw[j], b);
+      pr.out[(int64_t)(m0 + et) * n + n0 + ec] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    }
   }
 }
 
-template <int MT, bool GROUPED = false>
+template <int MT, int NF, bool GROUPED = false>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
   GemmArgs args = a;
   if (GROUPED && (a.ngroup < 1 || a.ngroup > kMaxGroup)) return hipErrorInvalidValue;
-  args.tiles_n = GROUPED ? a.g_tn_end[a.ngroup - 1] : (a.n + kSkinnyNW - 1) / kSkinnyNW;
+  int cols = (a.n + 16 * NF - 1) / (16 * NF);  // column blocks along x: the widest problem's
+  if (GROUPED)
+    for (int p = 0; p < a.ngroup; ++p) cols = std::max(cols, (a.g_n[p] + 16 * NF - 1) / (16 * NF));
+  args.tiles_n = cols;
   args.tiles_m = (a.m + 16 * MT - 1) / (16 * MT);
-  const int64_t wgs = (int64_t)args.tiles_m * args.tiles_n;
-  gemm_fp8_skinny<MT, GROUPED><<<dim3((unsigned)wgs), dim3(kSkinnyWaves * 64), 0, stream>>>(args);
+  const dim3 grid = GROUPED ? dim3((unsigned)args.tiles_n, (unsigned)a.ngroup, (unsigned)args.tiles_m)
+                            : dim3((unsigned)((int64_t)args.tiles_m * args.tiles_n));
+  gemm_fp8_skinny<MT, NF, GROUPED><<<grid, dim3(kSkinnyWaves * 64), 0, stream>>>(args);
   return hipGetLastError();
 }
 
@@ -1048,6 +1103,7 @@ const GemmConfig kConfigs[] = {
     {4, 64, 64, 4, 3, "bm64_bn64_w2x2_s3"},
     {5, 32, 16, 8, 0, "skinny_m32_n16_w8"},
     {6, 256, 256, 8, 2, "bm256_bn256_w2x4_s2_persistent"},
+    {7, 32, 32, 8, 0, "skinny_m32_n32_w8"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1078,8 +1134,9 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
     case 2: return launch<128, 256, 2, 4, 3, 128, 8>(a, stream);  // groups of 8: FFN-down 64.3 -> 63.4 us
     case 3: return launch<128, 128, 2, 2, 2, 128, 8>(a, stream);
     case 4: return launch<64, 64, 2, 2, 3, 128, 8>(a, stream);
-    case 5: return launch_skinny<2>(a, stream);
+    case 5: return launch_skinny<2, 1>(a, stream);
     case 6: return launch<256, 256, 2, 4, 2, 128, 4, false, kPersistOne>(a, stream, cus);
+    case 7: return launch_skinny<2, 2>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1087,11 +1144,11 @@ hipError_t launch_gemm(int id, int64_t m, int64_t n, int64_t k, const uint8_t* q
 hipError_t launch_gemm_group(int id, int64_t m, int64_t k, const uint8_t* qa, const float* a_scale, int nprob,
                              const GroupProblem* probs, int cus, hipStream_t stream) {
   if (nprob < 1 || nprob > kMaxGroup) return hipErrorInvalidValue;
-  if (id != 5 && id != 6) return hipErrorInvalidValue;
+  if (id != 5 && id != 6 && id != 7) return hipErrorInvalidValue;
   GemmArgs a{qa, a_scale, probs[0].qw, probs[0].w_scale, probs[0].bias, probs[0].out, (int)m, (int)probs[0].n,
              (int)k, 0, 0};
   a.ngroup = nprob;
-  const int cols = id == 6 ? 256 : kSkinnyNW;  // the form's column block
+  const int cols = id == 6 ? 256 : id == 7 ? 32 : 16;  // the form's column block
   int tn = 0;
   for (int p = 0; p < nprob; ++p) {
     tn += (int)((probs[p].n + cols - 1) / cols);
@@ -1102,7 +1159,8 @@ hipError_t launch_gemm_group(int id, int64_t m, int64_t k, const uint8_t* qa, co
     a.g_bias[p] = probs[p].bias;
     a.g_out[p] = probs[p].out;
   }
-  if (id == 5) return launch_skinny<2, true>(a, stream);
+  if (id == 5) return launch_skinny<2, 1, true>(a, stream);
+  if (id == 7) return launch_skinny<2, 2, true>(a, stream);
   return launch<256, 256, 2, 4, 2, 128, 4, false, kPersistGroup>(a, stream, cus);
 }
 

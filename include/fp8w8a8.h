@@ -225,9 +225,11 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
  * rounds of tiles over the CUs than the separate ones (or as many, all full), the GEMMs go
  * out as ONE persistent launch whose workgroups walk the tiles of all the problems (one
  * first prologue and one final output drain instead of nplans of each); when every plan
- * would run the skinny
- * configuration (5, a few tokens), as ONE launch over all the problems' channel blocks
- * (enough workgroups to fill the device, where one problem alone leaves it half idle);
+ * would run a skinny
+ * configuration (5 or 7, a few tokens), as ONE launch over all the problems' channel blocks
+ * (enough workgroups to fill the device, where one problem alone leaves it half idle; in
+ * configuration 7, 32 channels per workgroup, when their 16-channel blocks together
+ * outnumber the CUs);
  * otherwise each plan's GEMM runs as in fp8_linear_run. Outputs are bit-identical to the
  * separate calls either way.
  *

@@ -31,6 +31,10 @@ def _oracle_weight(w_cpu):
     return oq.quant_weights_per_channel(bf16_bits(w_cpu))
 
 
+def _cus(dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
 def _bias_bits(b):
     return None if b is None else bf16_bits(b)
 
@@ -60,6 +64,7 @@ TAIL_SHAPES = [(1, 16, 16), (26, 144, 48), (63, 16, 272), (65, 144, 16), (257, 1
 
 
 PERSISTENT = 6  # the 256 x 256 tiles walked by one workgroup per CU
+SKINNY, SKINNY_WIDE = 5, 7  # the weight stream, 16 and 32 channels per workgroup
 
 
 @pytest.mark.parametrize("config", range(N_CONFIGS))
@@ -272,8 +277,29 @@ def test_few_tokens_through_the_ffn_weights(config, m):
     layer, act = cfg["layers"][0]
     w, b = cfg["weights"][layer], cfg["biases"][layer]
     lin = Fp8Linear(w.to(dev), b.to(dev))
-    assert lin.config(m)[0] == 5
+    # 16-channel blocks of the 8192 FFN-up channels outnumber the CUs: the wide form
+    assert lin.config(m)[0] == (SKINNY_WIDE if w.shape[0] // 16 > _cus(dev) else SKINNY)
     _full_size_linear(cfg["activations"][act][:m].contiguous(), w, b, dev, f"{config} m={m}", lin=lin)
+
+
+@pytest.mark.parametrize("m", [1, 17, 26, 32])
+def test_wide_skinny_form_matches_the_narrow_one(m):
+    # configurations 5 and 7 (16 and 32 channels per workgroup) split k alike and sum in
+    # the same order: bit-identical outputs, here with ragged n (the last 32-channel block
+    # half valid) and ragged k, and both against the oracle element by element
+    dev = require_gpu()
+    n, k = 8208, 2064
+    case = make_case(m, n, k, seed=71 + m, kind="outlier")
+    qa, sa = oq.quant_rows(bf16_bits(case.a))
+    qw, sw = _oracle_weight(case.w)
+    ref = ol.linear_ref_fp8(qa, sa, qw, sw, _bias_bits(case.bias))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    args = (t(qa), t(sa), t(qw), t(sw), case.bias.to(dev))
+    narrow = gemm_run_config(SKINNY, *args)
+    wide = gemm_run_config(SKINNY_WIDE, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(narrow.view(torch.int16), wide.view(torch.int16)), f"m={m}"
+    assert_linear_close(wide, ref, f"wide skinny {m}x{n}x{k}")
 
 
 @pytest.fixture(scope="module")
@@ -330,7 +356,7 @@ def test_selector_picks_the_measured_best_at_the_page_shapes():
     assert down.config(4096)[0] == 2
     assert qkv.config(32760)[0] == PERSISTENT and down.config(32760)[0] == 0
     assert up.config(1024)[0] != PERSISTENT  # 128 tiles: one round
-    assert qkv.config(26)[0] == 5 and up.config(26)[0] == 5 and down.config(26)[0] == 5
+    assert qkv.config(26)[0] == SKINNY and down.config(26)[0] == SKINNY and up.config(26)[0] == SKINNY_WIDE
     assert qkv.config(64)[0] == 4
 
 

@@ -30,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 PERSISTENT = 6
 SKINNY = 5
+SKINNY_WIDE = 7  # the same weight stream with 32 channels per workgroup
 
 
 def _cus(dev):
@@ -116,14 +117,15 @@ def test_groups_of_one_and_of_four():
 
 @pytest.mark.parametrize("m", [1, 17, 26, 32])
 @pytest.mark.parametrize("a_kind", ["bf16", "e4m3"])
-def test_group_of_skinny_problems_in_one_launch(m, a_kind):
-    # a few tokens (the 26-row encoder input): every plan takes the skinny form, and the
-    # group runs as one launch over all the problems' 16-channel blocks
+@pytest.mark.parametrize("ns", [(4112, 1040, 2064), (1040, 2064, 528)])
+def test_group_of_skinny_problems_in_one_launch(m, a_kind, ns):
+    # a few tokens (the 26-row encoder input): every plan takes a skinny form, and the
+    # group runs as one launch over all the problems' column blocks (the wide form when
+    # their 16-channel blocks together outnumber the CUs: 451 blocks, else 227)
     dev = require_gpu()
     k = 2048
-    ns = (4112, 1040, 2064)
     lins, cases = _layers(ns, k, dev, seed=51, no_bias=(1,))
-    assert all(lin.config(m)[0] == SKINNY for lin in lins)
+    assert all(lin.config(m)[0] in (SKINNY, SKINNY_WIDE) for lin in lins)
     a = make_case(m, 16, k, seed=52, kind="outlier").a
     qa, sa = cref.quant_rows(bf16_bits(a))
     if a_kind == "bf16":
@@ -147,7 +149,7 @@ def test_group_falls_back_to_each_plans_own_launch(m):
     k = 2048
     lins, cases = _layers((4112, 1040), k, dev, seed=31)
     if m > 0 and _cus(dev) == 256:
-        assert lins[1].config(m)[0] not in (PERSISTENT, SKINNY)
+        assert lins[1].config(m)[0] not in (PERSISTENT, SKINNY, SKINNY_WIDE)
     a = make_case(max(m, 1), 16, k, seed=32, kind="outlier").a[:m]
     x = a.to(dev)
     separate = [lin(x) for lin in lins]
@@ -224,7 +226,7 @@ def test_group_replayed_from_a_graph_with_new_inputs(m):
     k = 2048
     lins, _ = _layers((4112, 4624), k, dev, seed=61, no_bias=(0,))
     if _cus(dev) == 256:
-        assert len({lin.config(m)[0] for lin in lins}) == 1 and lins[0].config(m)[0] in (SKINNY, PERSISTENT)
+        assert len({lin.config(m)[0] for lin in lins}) == 1 and lins[0].config(m)[0] in (SKINNY, SKINNY_WIDE, PERSISTENT)
     inputs = [make_case(m, 16, k, seed=62 + i, kind="outlier").a.to(dev) for i in range(3)]
     x = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((lins[0].workspace_bytes(m),), dtype=torch.uint8, device=dev)
