@@ -423,7 +423,10 @@ def block_bench(torch, fp8, lib, dev, stream, steps, config):
     res = {"quantisations": len(order), "gemms": len(lins), "steps": steps, "rounds": 5, "flop_per_step": flop,
            "ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
            "grouped": True, "ms_per_step_separate_gemms": round(ms_sep, 4),
-           "gemm_configs": {layer: lin.config(outs[layer].shape[0])[0] for layer, lin in lins.items()}}
+           "gemm_configs": {layer: lin.config(outs[layer].shape[0])[0] for layer, lin in lins.items()},
+           # the configuration of each activation's single grouped launch (-1: its layers' own GEMMs)
+           "group_configs": {name: fp8.group_config([lins[layer] for layer, _ in layers], layers[0][1])
+                             for name, layers in order}}
     del acts, codes, lins, outs
     torch.cuda.empty_cache()
     return res

@@ -21,6 +21,7 @@ from .ops import (  # noqa: F401
     gemm_config_count,
     gemm_run_config,
     linear,
+    group_config,
     linear_group,
     quant_gemm,
     quant_rows,
@@ -42,6 +43,7 @@ __all__ = [
     "quant_tensor",
     "dequant_tensor",
     "linear",
+    "group_config",
     "linear_group",
     "quant_rows",
     "quant_weights_per_channel",

@@ -68,6 +68,7 @@ SIGNATURES = {
     "fp8_linear_plan_config": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(_c_i64)]),
+    "fp8_linear_group_config": (ctypes.c_int, [_c_p, ctypes.c_int, _c_i64, ctypes.POINTER(ctypes.c_int)]),
     "fp8_gemm_config_count": (ctypes.c_int, []),
     "fp8_w8a16_create": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p, _c_p,
                                          ctypes.POINTER(_c_p)]),

@@ -500,6 +500,51 @@ int fp8_linear_run(const fp8_linear_plan* plan, int64_t m, const void* a, int a_
   return e == hipSuccess ? FP8W8A8_OK : FP8W8A8_ERR_HIP;
 }
 
+// The configuration of the single GEMM launch that fp8_linear_run_group makes for these
+// plans at m (config[i]: plan i's own choice at m), or -1 when each plan runs its own GEMM.
+static int group_launch_form(const fp8_linear_plan* const* plans, int nplans, int64_t m, const int* config) {
+  const fp8_linear_plan* p0 = plans[0];
+  // One launch for the group: when every plan takes a skinny form (in the wide one, 7, when
+  // the problems' 16-channel blocks together outnumber the CUs); or when every plan
+  // takes the 256 x 256 tiles (configuration 0, or its persistent form 6, which compute
+  // every tile alike) at a k where a single plan may take the persistent form, and one
+  // persistent launch needs fewer rounds of tiles over the CUs than the separate launches,
+  // or as many, all of them full. (Q, K and V at 8192 tokens: 256 tiles each, one round
+  // apiece, 768 together, three full rounds: 92.7 -> 84.9 us. At 6144 tokens, 192 tiles
+  // each: three rounds either way, the joint third a quarter full: 75.8 -> 79.5 us.)
+  int group_form = -1;  // the configuration of the one launch
+  if (nplans > 1) {
+    bool skinny = true, big_tiles = p0->k >= 2048 && p0->k <= 4096;
+    for (int i = 0; i < nplans; ++i) {
+      skinny = skinny && (config[i] == kW8A8Skinny || config[i] == kW8A8SkinnyWide);
+      big_tiles = big_tiles && (config[i] == 0 || config[i] == kW8A8Persistent);
+    }
+    if (skinny) {
+      // the joint grid takes the wide form when the 16-channel blocks of all the
+      // problems together exceed the CU count (the rule of a single plan, above)
+      int64_t blocks = 0;
+      for (int i = 0; i < nplans; ++i) blocks += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);
+      group_form = blocks > p0->cu_count ? kW8A8SkinnyWide : kW8A8Skinny;
+      // and the joint grid must fit as each plan's does
+      int64_t wgs = 0;
+      for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(group_form, m, plans[i]->n);
+      if (wgs * gemm_threads(group_form) >= kMaxGridThreads) group_form = -1;
+    } else if (big_tiles) {
+      const int64_t c = std::max(8, p0->cu_count / 8 * 8);  // the persistent grid
+      int64_t tiles = 0, rounds_apart = 0;
+      for (int i = 0; i < nplans; ++i) {
+        const int64_t t = gemm_workgroups(0, m, plans[i]->n);
+        tiles += t;
+        rounds_apart += (t + c - 1) / c;
+      }
+      const int64_t rounds_joint = (tiles + c - 1) / c;
+      if (rounds_joint < rounds_apart || (rounds_joint == rounds_apart && tiles % c == 0))
+        group_form = kW8A8Persistent;
+    }
+  }
+  return group_form;
+}
+
 int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_t m, const void* a, int a_kind,
                          const float* a_scale, void* const* outs_bf16, void* workspace, size_t workspace_bytes,
                          void* stream) {
@@ -535,45 +580,8 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
     config[i] = plan_bucket_config(plans[i], m);
     if (!grid_fits(config[i], m, plans[i]->n)) return FP8W8A8_ERR_BAD_SHAPE;
   }
-  // One launch for the group: when every plan takes a skinny form (in the wide one, 7, when
-  // the problems' 16-channel blocks together outnumber the CUs); or when every plan
-  // takes the 256 x 256 tiles (configuration 0, or its persistent form 6, which compute
-  // every tile alike) at a k where a single plan may take the persistent form, and one
-  // persistent launch needs fewer rounds of tiles over the CUs than the separate launches,
-  // or as many, all of them full. (Q, K and V at 8192 tokens: 256 tiles each, one round
-  // apiece, 768 together, three full rounds: 92.7 -> 84.9 us. At 6144 tokens, 192 tiles
-  // each: three rounds either way, the joint third a quarter full: 75.8 -> 79.5 us.)
-  bool grouped = false;
-  int group_form = -1;  // the configuration of the one launch
-  if (nplans > 1) {
-    bool skinny = true, big_tiles = p0->k >= 2048 && p0->k <= 4096;
-    for (int i = 0; i < nplans; ++i) {
-      skinny = skinny && (config[i] == kW8A8Skinny || config[i] == kW8A8SkinnyWide);
-      big_tiles = big_tiles && (config[i] == 0 || config[i] == kW8A8Persistent);
-    }
-    if (skinny) {
-      // the joint grid takes the wide form when the 16-channel blocks of all the
-      // problems together exceed the CU count (the rule of a single plan, above)
-      int64_t blocks = 0;
-      for (int i = 0; i < nplans; ++i) blocks += gemm_workgroups(kW8A8Skinny, m, plans[i]->n);
-      group_form = blocks > p0->cu_count ? kW8A8SkinnyWide : kW8A8Skinny;
-      // and the joint grid must fit as each plan's does
-      int64_t wgs = 0;
-      for (int i = 0; i < nplans; ++i) wgs += gemm_workgroups(group_form, m, plans[i]->n);
-      grouped = wgs * gemm_threads(group_form) < kMaxGridThreads;
-    } else if (big_tiles) {
-      const int64_t c = std::max(8, p0->cu_count / 8 * 8);  // the persistent grid
-      int64_t tiles = 0, rounds_apart = 0;
-      for (int i = 0; i < nplans; ++i) {
-        const int64_t t = gemm_workgroups(0, m, plans[i]->n);
-        tiles += t;
-        rounds_apart += (t + c - 1) / c;
-      }
-      const int64_t rounds_joint = (tiles + c - 1) / c;
-      grouped = rounds_joint < rounds_apart || (rounds_joint == rounds_apart && tiles % c == 0);
-      group_form = kW8A8Persistent;
-    }
-  }
+  const int group_form = group_launch_form(plans, nplans, m, config);
+  const bool grouped = group_form >= 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* qa = static_cast<const uint8_t*>(a);
   const float* sa = a_scale;
@@ -600,6 +608,22 @@ int fp8_linear_run_group(const fp8_linear_plan* const* plans, int nplans, int64_
                     p->cu_count, s) != hipSuccess)
       return FP8W8A8_ERR_HIP;
   }
+  return FP8W8A8_OK;
+}
+
+int fp8_linear_group_config(const fp8_linear_plan* const* plans, int nplans, int64_t m, int* config_id) {
+  if (!plans || !config_id) return FP8W8A8_ERR_INVALID_ARG;
+  if (nplans < 1 || nplans > FP8W8A8_MAX_GROUP) return FP8W8A8_ERR_INVALID_ARG;
+  for (int i = 0; i < nplans; ++i)
+    if (!plans[i]) return FP8W8A8_ERR_INVALID_ARG;
+  for (int i = 1; i < nplans; ++i) {
+    if (plans[i]->k != plans[0]->k) return FP8W8A8_ERR_BAD_SHAPE;
+    if (plans[i]->device != plans[0]->device) return FP8W8A8_ERR_BAD_DEVICE;
+  }
+  if (m < 0 || m >= FP8W8A8_MAX_ROWS) return FP8W8A8_ERR_BAD_SHAPE;
+  int config[FP8W8A8_MAX_GROUP];
+  for (int i = 0; i < nplans; ++i) config[i] = plan_bucket_config(plans[i], m);
+  *config_id = m == 0 ? -1 : group_launch_form(plans, nplans, m, config);
   return FP8W8A8_OK;
 }
 

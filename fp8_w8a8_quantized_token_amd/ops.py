@@ -272,6 +272,19 @@ class Fp8Linear:
     __call__ = forward
 
 
+def group_config(linears, m):
+    """The GEMM configuration of the single launch linear_group makes for these layers at m
+    tokens, or -1 when each layer runs its own GEMM (include/fp8w8a8.h,
+    fp8_linear_group_config)."""
+    linears = list(linears)
+    if not 1 <= len(linears) <= _lib.MAX_GROUP:
+        raise ValueError(f"a group takes 1..{_lib.MAX_GROUP} layers, got {len(linears)}")
+    plans = (ctypes.c_void_p * len(linears))(*[lin._plan.value for lin in linears])
+    cid = ctypes.c_int()
+    check(lib().fp8_linear_group_config(plans, len(linears), m, ctypes.byref(cid)), "fp8_linear_group_config")
+    return cid.value
+
+
 def linear_group(linears, x, x_scale=None, outs=None, workspace=None):
     """Several Fp8Linear layers on one input: [out_i [..., n_i]], bit-identical to
     [lin(x) for lin in linears], with x quantised once.

@@ -297,6 +297,19 @@ int fp8_linear(const void* a, int a_kind, const float* a_scale, int64_t m, int64
 int fp8_linear_plan_config(const fp8_linear_plan* plan, int64_t m, int* config_id, int* tile_m,
                            int* tile_n, int64_t* workgroups);
 
+/*
+ * fp8_linear_group_config writes the id of the GEMM kernel configuration of the single
+ * launch that fp8_linear_run_group makes for these plans at m rows (6: persistent 256 x
+ * 256 tiles over every problem; 5 or 7: the skinny weight stream over every problem's
+ * column blocks), or -1 when each plan runs its own GEMM (fp8_linear_plan_config then
+ * names each one; also for m == 0, which launches nothing). For tests and reports.
+ * Returns FP8W8A8_ERR_INVALID_ARG for a NULL array, element or output pointer or an
+ * nplans outside 1..FP8W8A8_MAX_GROUP, FP8W8A8_ERR_BAD_SHAPE for plans whose k differ
+ * or an m outside 0 <= m < FP8W8A8_MAX_ROWS, FP8W8A8_ERR_BAD_DEVICE for plans on
+ * different devices, as fp8_linear_run_group does.
+ */
+int fp8_linear_group_config(const fp8_linear_plan* const* plans, int nplans, int64_t m, int* config_id);
+
 /* Number of GEMM kernel configurations compiled in (ids 0 .. count-1). */
 int fp8_gemm_config_count(void);
 

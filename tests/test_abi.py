@@ -259,6 +259,22 @@ def test_run_group_validation(lib):
         assert g(arr(five), n, 4, A, _lib.A_BF16, None, arr(five), A, 1 << 20, None) == _lib.ERR_INVALID_ARG, n
 
 
+def test_group_config_validation(lib):
+    """The group-configuration query rejects NULL arrays, elements and outputs and a group
+    size outside 1..FP8W8A8_MAX_GROUP before it reads any plan."""
+    q = lib.fp8_linear_group_config
+    cid = ctypes.c_int(123)
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    arr = lambda x: ctypes.cast(x, ctypes.c_void_p)  # noqa: E731
+    assert q(None, 1, 4, ctypes.byref(cid)) == _lib.ERR_INVALID_ARG
+    assert q(arr(nulls), 2, 4, ctypes.byref(cid)) == _lib.ERR_INVALID_ARG
+    five = (ctypes.c_void_p * 5)(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED)
+    assert q(arr(five), 1, 4, None) == _lib.ERR_INVALID_ARG
+    for n in (0, -1, _lib.MAX_GROUP + 1):
+        assert q(arr(five), n, 4, ctypes.byref(cid)) == _lib.ERR_INVALID_ARG, n
+    assert cid.value == 123  # nothing written on an error
+
+
 def test_group_binding_rejects_bad_groups():
     from fp8_w8a8_quantized_token_amd import linear_group
 

@@ -21,7 +21,7 @@ from types import SimpleNamespace
 import pytest
 import torch
 
-from fp8_w8a8_quantized_token_amd import Fp8Linear, Fp8W8A8Error, _lib, linear_group, quant_rows
+from fp8_w8a8_quantized_token_amd import Fp8Linear, Fp8W8A8Error, _lib, group_config, linear_group, quant_rows
 from oracle import cref, linear as ol
 from tests._helpers import assert_codes_equal, assert_linear_close, require_gpu
 from workloads import bf16_bits, make_case, make_config
@@ -138,6 +138,24 @@ def test_group_of_skinny_problems_in_one_launch(m, a_kind, ns):
     for i, (g, s) in enumerate(zip(grouped, separate)):
         assert torch.equal(_bits(g), _bits(s)), f"m={m} problem {i}"
     _check_rows_against_oracle(grouped, cases, qa, sa, f"skinny group m={m}")
+
+
+def test_group_reports_its_launch_form():
+    # the configuration of the one launch, as the run takes it: the Q/K/V weights at 32760
+    # tokens as one persistent launch, their 26-row encoder input as one wide skinny launch
+    # (384 16-channel blocks on 256 CUs), a narrow skinny group (227 blocks) in
+    # configuration 5, and a narrow weight next to a wide one at 700 tokens as separate GEMMs
+    dev = require_gpu()
+    if _cus(dev) != 256:
+        pytest.skip("the forms are chosen for a 256-CU device")
+    qkv, _ = _layers((2048, 2048, 2048), 2048, dev, seed=81)
+    assert group_config(qkv, 32760) == PERSISTENT
+    assert group_config(qkv, 26) == SKINNY_WIDE
+    assert group_config(qkv[:1], 26) == -1 and group_config(qkv, 0) == -1
+    narrow, _ = _layers((1040, 2064, 528), 2048, dev, seed=82)
+    assert group_config(narrow, 26) == SKINNY
+    mixed, _ = _layers((4112, 1040), 2048, dev, seed=83)
+    assert group_config(mixed, 700) == -1
 
 
 @pytest.mark.parametrize("m", [0, 700, 3000, 8200])
