@@ -184,8 +184,10 @@ constexpr int kW8A8Skinny = 5;
 // > 256 MB of rotating weights, random codes, m = 26, k = 2048): 384 workgroups of
 // configuration 5 (n = 6144, the grid of the Q/K/V encoder group) 8.00 -> 6.95 us, 512
 // (n = 8192) 8.29 -> 7.31; at 256 or fewer it loses (n = 4096: 5.87 against 7.21 us, n =
-// 2048: 5.16 against 6.57, k = 8192: 12.7 against 17.1). So it serves the skinny products
-// whose configuration-5 grid exceeds the CU count.
+// 2048: 5.16 against 6.57, k = 8192: 12.7 against 17.1), and the step is at the CU count:
+// 256 workgroups of configuration 5 (n = 4096) 5.57 us, 272 (n = 4352) 7.77, against 6.6
+// for configuration 7 at both. So it serves the skinny products whose configuration-5 grid
+// exceeds the CU count.
 constexpr int kW8A8SkinnyWide = 7;
 // The persistent form of the 256 x 256 tiles (one workgroup per CU walking its tiles, the
 // next tile's first stages requested before the current tile's epilogue) is output-for-
